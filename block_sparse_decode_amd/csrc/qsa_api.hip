@@ -1,0 +1,249 @@
+// qsa_api.hip -- the C ABI of libqsa (declared in include/qsa.h): host-side validation,
+// launch-shape choice and kernel launches. No allocation, no synchronisation, no global state.
+#include <math.h>
+#include <algorithm>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qsa_internal.hpp"
+
+using namespace qsa;
+
+namespace {
+
+constexpr int kMaxRows = 4;
+constexpr int kMaxPages = 4096;
+constexpr int kMaxKW = 256;
+constexpr int kMaxCols = 64;
+constexpr int kMaxSplits = 64;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+qsa_status check_shape(const qsa_shape *sh)
+{
+    if (!sh) return QSA_ERR_INVALID_ARG;
+    if (sh->num_requests < 0 || sh->num_rows < 0 || sh->num_q_heads < 1 || sh->num_kv_heads < 1 ||
+        sh->num_q_heads % sh->num_kv_heads != 0 || sh->max_pages < 1 || sh->num_phys_pages < 0 ||
+        sh->topk < 0 || sh->window < 0 || sh->max_rows_per_request < 1 || !isfinite(sh->sm_scale))
+        return QSA_ERR_INVALID_ARG;
+    if (sh->max_rows_per_request > kMaxRows) return QSA_ERR_UNSUPPORTED;
+    if (sh->head_dim != 64 && sh->head_dim != 128) return QSA_ERR_UNSUPPORTED;
+    if (sh->page_size != 64 && sh->page_size != 128) return QSA_ERR_UNSUPPORTED;
+    if (sh->max_pages > kMaxPages) return QSA_ERR_UNSUPPORTED;
+    if ((int64_t)sh->topk + sh->window > kMaxKW) return QSA_ERR_UNSUPPORTED;
+    if (sh->num_requests > 65535 || sh->num_kv_heads > 65535) return QSA_ERR_UNSUPPORTED;
+    if (sh->num_rows > (int64_t)sh->num_requests * sh->max_rows_per_request) return QSA_ERR_INVALID_ARG;
+    return QSA_OK;
+}
+
+qsa_status check_rows_ptrs(const qsa_paged *pg)
+{
+    if (!pg || !pg->seq_lens || !pg->row_offsets) return QSA_ERR_INVALID_ARG;
+    if (!aligned16(pg->seq_lens) || !aligned16(pg->row_offsets)) return QSA_ERR_INVALID_ARG;
+    if (pg->error_word && ((uintptr_t)pg->error_word & 3u)) return QSA_ERR_INVALID_ARG;
+    return QSA_OK;
+}
+
+int col_tiles(const qsa_shape *sh)
+{
+    const int cols = sh->max_rows_per_request * (sh->num_q_heads / sh->num_kv_heads);
+    return cols <= 16 ? 1 : cols <= 32 ? 2 : 4;
+}
+
+// Splits per (request, KV head) when the caller leaves the choice to the library: enough
+// workgroups to give each of the 256 CUs about three, without splits so thin that a wave
+// gets fewer than two pages of the expected union.
+int auto_splits(const qsa_shape *sh)
+{
+    const int64_t base = (int64_t)sh->num_requests * sh->num_kv_heads;
+    if (base <= 0) return 1;
+    const int64_t union_est = std::min<int64_t>((int64_t)sh->max_rows_per_request * (sh->topk + sh->window),
+                                                sh->max_pages);
+    int64_t s = (768 + base - 1) / base;
+    const int64_t cap = std::max<int64_t>(1, union_est / (2 * kDecodeWaves));
+    s = std::min(s, cap);
+    s = std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits));
+    return (int)s;
+}
+
+int resolve_splits(const qsa_shape *sh, int32_t num_splits)
+{
+    if (num_splits <= 0) return auto_splits(sh);
+    return num_splits > kMaxSplits ? kMaxSplits : num_splits;
+}
+
+size_t decode_ws_bytes(const qsa_shape *sh, int splits)
+{
+    if (splits <= 1) return 0;
+    const size_t per = (size_t)sh->num_rows * sh->num_q_heads;
+    const size_t o = (size_t)splits * per * sh->head_dim * sizeof(float);
+    const size_t ml = (size_t)splits * per * 2 * sizeof(float);
+    return ((o + 255) & ~(size_t)255) + ml;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char *qsa_status_string(qsa_status st)
+{
+    switch (st) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_INVALID_ARG: return "invalid argument";
+    case QSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case QSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case QSA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+qsa_status qsa_index_scores(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, float *scores,
+                            void *stream)
+{
+    qsa_status st = check_shape(sh);
+    if (st != QSA_OK) return st;
+    if ((st = check_rows_ptrs(pg)) != QSA_OK) return st;
+    if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
+    if (!q || !scores || !pg->page_table || !pg->index_keys) return QSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(scores) || !aligned16(pg->page_table) || !aligned16(pg->index_keys))
+        return QSA_ERR_INVALID_ARG;
+    IndexParams prm;
+    prm.page_table = pg->page_table;
+    prm.seq_lens = pg->seq_lens;
+    prm.row_offsets = pg->row_offsets;
+    prm.keys = pg->index_keys;
+    prm.q32 = reinterpret_cast<const uint32_t *>(q);
+    prm.scores = scores;
+    prm.err = pg->error_word;
+    prm.NP = sh->num_phys_pages;
+    prm.N = sh->num_rows;
+    prm.MP = sh->max_pages;
+    prm.P = sh->page_size;
+    prm.W = sh->window;
+    prm.Hq = sh->num_q_heads;
+    prm.Hkv = sh->num_kv_heads;
+    prm.rmax = sh->max_rows_per_request;
+    prm.sm_scale = sh->sm_scale;
+    hipError_t e = launch_index_scores(prm, sh->head_dim, sh->num_requests, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+qsa_status qsa_select_topk(const qsa_shape *sh, const qsa_paged *pg, const float *scores, int32_t *selected,
+                           void *stream)
+{
+    qsa_status st = check_shape(sh);
+    if (st != QSA_OK) return st;
+    if ((st = check_rows_ptrs(pg)) != QSA_OK) return st;
+    if (sh->num_rows == 0 || sh->num_requests == 0 || sh->topk + sh->window == 0) return QSA_OK;
+    if (!scores || !selected || !aligned16(scores) || !aligned16(selected)) return QSA_ERR_INVALID_ARG;
+    SelectParams prm;
+    prm.seq_lens = pg->seq_lens;
+    prm.row_offsets = pg->row_offsets;
+    prm.scores = scores;
+    prm.selected = selected;
+    prm.err = pg->error_word;
+    prm.N = sh->num_rows;
+    prm.MP = sh->max_pages;
+    prm.P = sh->page_size;
+    prm.k = sh->topk;
+    prm.W = sh->window;
+    prm.rmax = sh->max_rows_per_request;
+    hipError_t e = launch_select_topk(prm, sh->num_requests, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+size_t qsa_workspace_bytes(const qsa_shape *sh, int32_t num_splits)
+{
+    if (check_shape(sh) != QSA_OK) return 0;
+    if (sh->max_rows_per_request * (sh->num_q_heads / sh->num_kv_heads) > kMaxCols) return 0;
+    return decode_ws_bytes(sh, resolve_splits(sh, num_splits));
+}
+
+qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const int32_t *selected,
+                             uint16_t *out, float *lse, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    qsa_status st = check_shape(sh);
+    if (st != QSA_OK) return st;
+    if ((st = check_rows_ptrs(pg)) != QSA_OK) return st;
+    if (sh->max_rows_per_request * (sh->num_q_heads / sh->num_kv_heads) > kMaxCols) return QSA_ERR_UNSUPPORTED;
+    if (num_splits < 0) return QSA_ERR_INVALID_ARG;
+    if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
+    if (!q || !out || !pg->page_table || !pg->k_codes || !pg->k_scales || !pg->v_codes || !pg->v_scales)
+        return QSA_ERR_INVALID_ARG;
+    if (sh->topk + sh->window > 0 && !selected) return QSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(pg->page_table) || !aligned16(pg->k_codes) ||
+        !aligned16(pg->k_scales) || !aligned16(pg->v_codes) || !aligned16(pg->v_scales) ||
+        (selected && !aligned16(selected)) || (lse && !aligned16(lse)))
+        return QSA_ERR_INVALID_ARG;
+    if (!isfinite(pg->k_global) || !isfinite(pg->v_global)) return QSA_ERR_INVALID_ARG;
+    const int splits = resolve_splits(sh, num_splits);
+    const size_t need = decode_ws_bytes(sh, splits);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return QSA_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned16(workspace)) return QSA_ERR_INVALID_ARG;
+    }
+    DecodeParams prm;
+    prm.page_table = pg->page_table;
+    prm.seq_lens = pg->seq_lens;
+    prm.row_offsets = pg->row_offsets;
+    prm.k_codes = pg->k_codes;
+    prm.k_scales = pg->k_scales;
+    prm.v_codes = pg->v_codes;
+    prm.v_scales = pg->v_scales;
+    prm.q = q;
+    prm.selected = selected;
+    prm.out = out;
+    prm.lse = lse;
+    prm.part_o = need ? reinterpret_cast<float *>(workspace) : nullptr;
+    prm.part_ml = nullptr;
+    if (need) {
+        const size_t per = (size_t)sh->num_rows * sh->num_q_heads;
+        const size_t o = (size_t)splits * per * sh->head_dim * sizeof(float);
+        prm.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + ((o + 255) & ~(size_t)255));
+    }
+    prm.err = pg->error_word;
+    prm.NP = sh->num_phys_pages;
+    prm.N = sh->num_rows;
+    prm.MP = sh->max_pages;
+    prm.P = sh->page_size;
+    prm.KW = sh->topk + sh->window;
+    prm.Hq = sh->num_q_heads;
+    prm.Hkv = sh->num_kv_heads;
+    prm.rmax = sh->max_rows_per_request;
+    prm.splits = splits;
+    prm.qk_scale_log2 = (float)((double)sh->sm_scale * (double)pg->k_global * 1.4426950408889634);
+    prm.v_global = pg->v_global;
+    hipError_t e = launch_sparse_decode(prm, sh->head_dim, sh->num_requests, col_tiles(sh), (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+qsa_status qsa_nvfp4_dequant_pages(const qsa_shape *sh, const uint8_t *codes, const uint8_t *scales,
+                                   float global_scale, const int32_t *pages, int32_t num_pages, float *out,
+                                   void *stream)
+{
+    if (!sh) return QSA_ERR_INVALID_ARG;
+    if (sh->num_kv_heads < 1 || sh->num_phys_pages < 0 || num_pages < 0 || !isfinite(global_scale))
+        return QSA_ERR_INVALID_ARG;
+    if (sh->head_dim != 64 && sh->head_dim != 128) return QSA_ERR_UNSUPPORTED;
+    if (sh->page_size != 64 && sh->page_size != 128) return QSA_ERR_UNSUPPORTED;
+    if (num_pages == 0) return QSA_OK;
+    if (!codes || !scales || !pages || !out) return QSA_ERR_INVALID_ARG;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(pages) || !aligned16(out)) return QSA_ERR_INVALID_ARG;
+    DequantParams prm;
+    prm.codes = codes;
+    prm.scales = scales;
+    prm.pages = pages;
+    prm.out = out;
+    prm.NP = sh->num_phys_pages;
+    prm.n = num_pages;
+    prm.Hkv = sh->num_kv_heads;
+    prm.P = sh->page_size;
+    prm.global = global_scale;
+    hipError_t e = launch_dequant_pages(prm, sh->head_dim, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// qsa_device.hpp -- device helpers shared by the gfx950 kernels of libqsa.
+//
+// Formats (OCP specs): e2m1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit),
+// E4M3FN block scales (bias 7, NaN at S.1111.111, no infinities), bf16 queries and keys.
+// The NVFP4 KV cache of the pages stores "uint8 e2m1 pages + e4m3 block scales"
+// (TensorRT-LLM PR #20276, Features, NVFP4 KV cache row).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+typedef _Float16 half_t;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// E4M3FN scale byte -> f16. gfx950's fp8 convert decodes the OCP E4M3FN format
+// (all 256 codes, NaN included). Every E4M3FN value, from the 2^-9 subnormal up to 448,
+// is exact in f16, so the second conversion is exact too.
+__device__ __forceinline__ half_t e4m3_to_f16(uint32_t byte)
+{
+    float f = __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+    return (half_t)f;
+}
+
+// Eight e2m1 codes (one dword; element 2i in the low nibble of byte i) times one e4m3
+// block scale -> eight f16 values, exactly.
+// The hardware fp4 convert takes its scale operand's exponent only, so it runs with
+// scale 1.0 and returns the exact e2m1 values. The block scale is then one packed f16
+// multiply per pair. An e2m1 value (<= 2 significant bits) times an e4m3 value
+// (<= 4 bits) needs at most 6 bits and lies in [2^-10, 2688], so the product is exact
+// in f16.
+__device__ __forceinline__ f16x8 nvfp4_dequant8(uint32_t codes, half_t s)
+{
+    const f16x2 ss = {s, s};
+    f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
+    f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
+    f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
+    f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
+    return (f16x8){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key), with -0 == +0.
+__device__ __forceinline__ uint32_t float_order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ void set_error(uint32_t *err, uint32_t bit)
+{
+    if (err) atomicOr(err, bit);
+}
+
+// Row geometry of an MTP verify batch: row j of a request with R rows and L_b tokens
+// sees L_b - (R - 1 - j) tokens (clipped at 0) and ceil(L / P) pages (clipped at MP).
+struct RowGeom {
+    int64_t len;
+    int pages;
+};
+
+__device__ __forceinline__ RowGeom row_geom(int64_t seq_len, int R, int j, int P, int MP)
+{
+    RowGeom g;
+    int64_t L = seq_len - (int64_t)(R - 1 - j);
+    if (L < 0) L = 0;
+    int64_t n = (L + P - 1) / P;
+    g.len = L;
+    g.pages = (int)(n < MP ? n : MP);
+    return g;
+}
+
+// Rows [r0, r0 + R) of one request, clipped to [0, N) and to at most rmax rows. A clip
+// means row_offsets broke its contract; the caller learns it through the error word.
+__device__ __forceinline__ int clip_rows(int r0, int r1, int N, int rmax, uint32_t *err, bool report)
+{
+    int R = r1 - r0;
+    bool bad = r0 < 0 || R < 0 || r1 > N || R > rmax;
+    if (r0 < 0 || R <= 0) R = 0;
+    else {
+        if (r0 + R > N) R = N - r0 > 0 ? N - r0 : 0;
+        if (R > rmax) R = rmax;
+    }
+    if (bad && report) set_error(err, QSA_DEVERR_ROWS);
+    return R;
+}
+
+// Wave-wide reductions over the lanes that share a 16-lane column slot (xor 16, xor 32).
+__device__ __forceinline__ float max_across_groups(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+__device__ __forceinline__ float sum_across_groups(float v)
+{
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Block-wide exclusive prefix sum of one uint32 per thread (blockDim.x = NT, a multiple
+// of 64). `tmp` holds NT / 64 + 1 words of LDS. Returns the exclusive prefix; *total gets
+// the block sum. Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t *total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        uint32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t acc = 0;
+        for (int w = 0; w < NT / 64; ++w) {
+            uint32_t t = tmp[w];
+            tmp[w] = acc;
+            acc += t;
+        }
+        tmp[NT / 64] = acc;
+    }
+    __syncthreads();
+    uint32_t res = tmp[wave] + x - v;
+    *total = tmp[NT / 64];
+    __syncthreads();
+    return res;
+}
+
+}  // namespace qsa

@@ -1,0 +1,72 @@
+// qsa_internal.hpp -- launch parameter blocks shared by the host API and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+struct IndexParams {
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    const int32_t *row_offsets;
+    const uint16_t *keys;
+    const uint32_t *q32;      // bf16 pairs
+    float *scores;
+    uint32_t *err;
+    int64_t NP;
+    int N, MP, P, W, Hq, Hkv, rmax;
+    float sm_scale;
+};
+
+struct SelectParams {
+    const int32_t *seq_lens;
+    const int32_t *row_offsets;
+    const float *scores;
+    int32_t *selected;
+    uint32_t *err;
+    int N, MP, P, k, W, rmax;
+};
+
+struct DecodeParams {
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    const int32_t *row_offsets;
+    const uint8_t *k_codes;
+    const uint8_t *k_scales;
+    const uint8_t *v_codes;
+    const uint8_t *v_scales;
+    const uint16_t *q;
+    const int32_t *selected;
+    uint16_t *out;
+    float *lse;
+    float *part_o;            // [S][N][Hq][D] unnormalised partial outputs (S > 1)
+    float *part_ml;           // [S][N][Hq][2] (max in log2 units, sum)
+    uint32_t *err;
+    int64_t NP;
+    int N, MP, P, KW, Hq, Hkv, rmax, splits;
+    float qk_scale_log2;      // sm_scale * k_global * log2(e)
+    float v_global;
+};
+
+struct DequantParams {
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const int32_t *pages;
+    float *out;
+    int64_t NP;
+    int n, Hkv, P;
+    float global;
+};
+
+hipError_t launch_index_scores(const IndexParams &prm, int D, int B, hipStream_t stream);
+hipError_t launch_select_topk(const SelectParams &prm, int B, hipStream_t stream);
+hipError_t launch_sparse_decode(const DecodeParams &prm, int D, int B, int ncol_tiles, hipStream_t stream);
+hipError_t launch_dequant_pages(const DequantParams &prm, int D, hipStream_t stream);
+
+// number of waves per decode workgroup
+constexpr int kDecodeWaves = 4;
+
+}  // namespace qsa

@@ -1,0 +1,189 @@
+/*
+ * qsa.h -- C ABI of the query-sparse NVFP4 decode / verify attention library (libqsa.so).
+ *
+ * The method (TensorRT-LLM PR #20276, "What runs on the fast paths"; PR #20937,
+ * Description > What changes) runs one attention layer of a decode or MTP-verify step
+ * over a paged KV cache in three calls:
+ *
+ *   1. qsa_index_scores  -- score every page of every query row against its index key;
+ *   2. qsa_select_topk   -- canonical top-k pages plus a local window per row;
+ *   3. qsa_sparse_decode -- split-KV softmax attention over the selected pages, with an
+ *                           LSE merge of the splits.
+ *
+ * Conventions shared by every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or reads device memory from the host, and it never synchronises.
+ *     Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Pointers must be aligned to 16 bytes.
+ *   - Host-checkable argument errors return a status before any launch. Nothing is
+ *     written then. The library never aborts or throws.
+ *   - The library keeps no mutable global state. Calls on different streams may run
+ *     concurrently as long as their output buffers are distinct.
+ *   - Data-dependent preconditions (page ids, lengths) cannot be checked on the host
+ *     without a sync. Device code handles a violation as stated per call, and if
+ *     `paged->error_word` is non-NULL it ORs one of the QSA_DEVERR_* bits into it.
+ *
+ * Notation: B requests, N = row_offsets[B] query rows, Hq query heads, Hkv KV heads
+ * (G = Hq / Hkv), d head dim, P tokens per page, MP page-table stride, NP physical pages,
+ * k top-k, W window pages.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+
+typedef enum qsa_status {
+    QSA_OK = 0,
+    QSA_ERR_INVALID_ARG = 1,          /* NULL required pointer, negative or inconsistent size */
+    QSA_ERR_UNSUPPORTED = 2,          /* a size outside what the kernels are built for */
+    QSA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < qsa_workspace_bytes(...) */
+    QSA_ERR_HIP = 4                   /* the HIP runtime reported an error at launch */
+} qsa_status;
+
+/* Bits OR-ed into *error_word by device code (sticky until the caller clears them). */
+#define QSA_DEVERR_PAGE_ID    0x1u   /* a page-table entry outside [-1, NP): treated as -1 */
+#define QSA_DEVERR_SEQ_LEN    0x2u   /* seq_lens[b] < rows of b, or > MP * P: rows clipped */
+#define QSA_DEVERR_ROWS       0x4u   /* row_offsets not non-decreasing, or a request with > max rows */
+#define QSA_DEVERR_Q_RANGE    0x8u   /* a q element beyond the f16 range (|q| > 65504) */
+#define QSA_DEVERR_SELECTED   0x10u  /* a selected entry outside [-1, MP): ignored */
+
+/* Sizes of one call. Host memory, read during the call only. */
+typedef struct qsa_shape {
+    int32_t num_requests;          /* B >= 0 */
+    int32_t num_rows;              /* N = row_offsets[B] >= 0 (the caller knows it) */
+    int32_t max_rows_per_request;  /* 1..4: upper bound on row_offsets[b+1] - row_offsets[b] */
+    int32_t num_q_heads;           /* Hq >= 1, a multiple of Hkv */
+    int32_t num_kv_heads;          /* Hkv >= 1 */
+    int32_t head_dim;              /* d: 64 or 128 */
+    int32_t page_size;             /* P: 64 or 128 tokens */
+    int32_t max_pages;             /* MP: page-table row stride, 1..4096 */
+    int64_t num_phys_pages;        /* NP >= 0: pages in each pool plane */
+    int32_t topk;                  /* k >= 0 */
+    int32_t window;                /* W >= 0, k + W <= 256 */
+    float   sm_scale;              /* softmax scale, normally (float)(1 / sqrt(d)) */
+} qsa_shape;
+
+/*
+ * The paged KV cache. One physical page index addresses every plane (PR #20276, Features,
+ * NVFP4 KV cache: the data and scale pools keep one page index). Device memory.
+ *   page_table  int32 [B][MP]           logical page -> physical page, -1 = no page
+ *   seq_lens    int32 [B]               tokens of request b, including this step's rows
+ *   row_offsets int32 [B+1]             rows of request b are [row_offsets[b], row_offsets[b+1])
+ *   k_codes     uint8 [NP][Hkv][P][d/2] e2m1 codes, element 2i in the low nibble of byte i
+ *   k_scales    uint8 [NP][Hkv][P][d/16] OCP E4M3FN scale of elements [16j, 16j+16)
+ *   v_codes, v_scales                   as for K
+ *   index_keys  bf16  [NP][Hkv][d]      per-page index key (only qsa_index_scores reads it)
+ *   k_global, v_global                  fp32 per-tensor scales: K = e2m1 * e4m3 * k_global
+ *   error_word  uint32 (device), optional: QSA_DEVERR_* bits are OR-ed into it
+ */
+typedef struct qsa_paged {
+    const int32_t  *page_table;
+    const int32_t  *seq_lens;
+    const int32_t  *row_offsets;
+    const uint8_t  *k_codes;
+    const uint8_t  *k_scales;
+    const uint8_t  *v_codes;
+    const uint8_t  *v_scales;
+    const uint16_t *index_keys;
+    float           k_global;
+    float           v_global;
+    uint32_t       *error_word;
+} qsa_paged;
+
+/*
+ * Index scores (PR #20276, "What runs on the fast paths": index store and compression,
+ * then index scores; PR #20937, MTP > Verify: request-tiled index scores).
+ *   q       bf16 [N][Hq][d]   (device)
+ *   scores  fp32 [N][MP]      (device, written in full)
+ * Row j of request b (R_b rows) sees L = seq_lens[b] - (R_b - 1 - j) tokens and
+ * n = min(ceil(L / P), MP) pages. For every candidate column p < n - W whose page-table
+ * entry is valid:
+ *   scores[row][p] = fl32(sm_scale * max_h dot_h),
+ *   dot_h = sum_{i ascending} q[row][h][i] * index_keys[phys][h / G][i],
+ * with the sum in fp32, rounded after each addition. A zero score is stored as +0.
+ * Every other column is -inf. The result is bitwise reproducible.
+ * Reads page_table, seq_lens, row_offsets, index_keys.
+ */
+qsa_status qsa_index_scores(const qsa_shape *shape, const qsa_paged *paged,
+                            const uint16_t *q, float *scores, void *stream);
+
+/*
+ * Canonical top-k selection plus local window (PR #20276, Features, "Canonical QSA
+ * selection": the selection row is a pure function of the scores, the window and k,
+ * taking every block strictly above the k-th score with ties to the highest index;
+ * Decisions worth knowing: the result must not depend on launch order).
+ *   scores    fp32  [N][MP]     (device)
+ *   selected  int32 [N][k + W]  (device, written in full)
+ * Per row (n as above): the window is pages [max(0, n - W), n). Candidates are columns
+ * p < n - W whose score is neither NaN nor -inf. The row keeps the first min(k, |C|)
+ * candidates by (score descending, page index descending), -0 equal to +0, adds the
+ * window, and stores them in ascending order followed by -1 padding. Bitwise deterministic.
+ * Reads seq_lens and row_offsets (not the page table and not the pools).
+ */
+qsa_status qsa_select_topk(const qsa_shape *shape, const qsa_paged *paged,
+                           const float *scores, int32_t *selected, void *stream);
+
+/*
+ * Workspace needed by qsa_sparse_decode for `num_splits` (0 = the library's choice for
+ * this shape). Returns 0 when the call needs none. Also 0 for an invalid shape.
+ */
+size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
+
+/*
+ * Split-KV sparse GQA attention over the selected pages, with an LSE merge (PR #20937,
+ * What changes: a split-K + merge decode kernel with a lean one-split variant;
+ * request-grouped verify attention with a per-row merge).
+ *   q          bf16  [N][Hq][d]     (device)
+ *   selected   int32 [N][k + W]     (device; entries outside [0, MP) are ignored, and
+ *                                    a page listed twice counts once)
+ *   out        bf16  [N][Hq][d]     (device, written in full, RNE)
+ *   lse        fp32  [N][Hq]        (device, optional: natural-log sum of exp of the logits)
+ *   num_splits 0 = the library's choice; > 0 forces that many KV splits per
+ *              (request, KV head), clamped to 64
+ *   workspace  device scratch of at least qsa_workspace_bytes(shape, num_splits) bytes;
+ *              its contents on entry do not matter
+ * For row j of request b and q head h, the tokens attended are
+ *   T = {(p, t): p listed in the row, page_table[b][p] valid, t < P, p * P + t < L}.
+ * The output is softmax(sm_scale * k_global * q . K_raw) @ (v_global * V_raw) over T, where
+ * K_raw and V_raw are e2m1 * e4m3. An empty T gives out = 0 and lse = -inf. Each request's
+ * rows share one read of the union of their selected pages. fp32 accumulation; the q and
+ * P operands of the MFMA tiles are f16 (q must lie in the f16 range; see QSA_DEVERR_Q_RANGE).
+ * Deterministic for a fixed num_splits.
+ */
+qsa_status qsa_sparse_decode(const qsa_shape *shape, const qsa_paged *paged,
+                             const uint16_t *q, const int32_t *selected,
+                             uint16_t *out, float *lse, int32_t num_splits,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Parity hook: NVFP4 dequantisation of whole pages through the same device decode that
+ * qsa_sparse_decode uses (the counterpart of the pages' NVFP4 page -> bf16 conversion,
+ * PR #20937, qsa_nvfp4_pages_to_bf16).
+ *   codes  uint8 [NP][Hkv][P][d/2], scales uint8 [NP][Hkv][P][d/16]   (device)
+ *   pages  int32 [num_pages] physical page ids (device; an id outside [0, NP) gives NaN rows)
+ *   out    fp32  [num_pages][Hkv][P][d] = fl32(e2m1 * e4m3 * global)  (device)
+ * Uses shape->num_kv_heads, head_dim, page_size and num_phys_pages.
+ */
+qsa_status qsa_nvfp4_dequant_pages(const qsa_shape *shape, const uint8_t *codes,
+                                   const uint8_t *scales, float global_scale,
+                                   const int32_t *pages, int32_t num_pages, float *out,
+                                   void *stream);
+
+/* Static description of a status code. Never NULL. */
+const char *qsa_status_string(qsa_status status);
+
+/* QSA_ABI_VERSION of the loaded library. */
+int32_t qsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/qsa.h declares, and its struct layouts match the ctypes mirrors. Host-side
+argument validation rejects bad calls before any launch (these calls never reach HIP).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_decode_amd as q
+from block_sparse_decode_amd import Paged, Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = q.lib()
+    declared = _declared_functions()
+    assert declared == sorted(q.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True, check=True)
+    syms = set(l.split()[-1] for l in out.stdout.splitlines() if l.strip())
+    for name in declared:
+        assert name in syms, name
+        assert hasattr(L, name)
+
+
+def test_abi_version_and_status_strings():
+    assert q.qsa_abi_version() == 1
+    for st, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
+                     (3, "workspace too small"), (4, "HIP launch error"), (99, "unknown status")]:
+        assert q.qsa_status_string(st) == text
+
+
+def test_struct_layout_matches_header(tmp_path):
+    prog = tmp_path / "layout.c"
+    prog.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "qsa.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu\n", sizeof(qsa_shape), offsetof(qsa_shape, num_phys_pages),
+         offsetof(qsa_shape, topk), offsetof(qsa_shape, sm_scale), sizeof(qsa_paged));
+  printf("%zu %zu %zu %zu\n", offsetof(qsa_paged, index_keys), offsetof(qsa_paged, k_global),
+         offsetof(qsa_paged, v_global), offsetof(qsa_paged, error_word));
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
+    a, b = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")[:2]
+    want_a = [ctypes.sizeof(Shape), Shape.num_phys_pages.offset, Shape.topk.offset, Shape.sm_scale.offset,
+              ctypes.sizeof(Paged)]
+    want_b = [Paged.index_keys.offset, Paged.k_global.offset, Paged.v_global.offset, Paged.error_word.offset]
+    assert list(map(int, a.split())) == want_a
+    assert list(map(int, b.split())) == want_b
+
+
+def _shape(**kw):
+    base = dict(num_requests=2, num_rows=8, max_rows_per_request=4, num_q_heads=32, num_kv_heads=4,
+                head_dim=128, page_size=64, max_pages=512, num_phys_pages=1024, topk=32, window=2,
+                sm_scale=0.088388)
+    base.update(kw)
+    return Shape(**base)
+
+
+FAKE = 0x1000     # a 16-byte aligned, never dereferenced address: every call below fails validation first
+
+
+def _paged(**kw):
+    base = dict(page_table=FAKE, seq_lens=FAKE, row_offsets=FAKE, k_codes=FAKE, k_scales=FAKE, v_codes=FAKE,
+                v_scales=FAKE, index_keys=FAKE, k_global=1.0, v_global=1.0, error_word=None)
+    base.update(kw)
+    return Paged(**base)
+
+
+def _raw(name, *args):
+    return getattr(q.lib(), name)(*args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 2), (dict(head_dim=256), 2), (dict(page_size=32), 2), (dict(max_pages=4097), 2),
+    (dict(topk=250, window=7), 2), (dict(max_rows_per_request=5), 2),
+    (dict(num_q_heads=30), 1), (dict(num_kv_heads=0), 1), (dict(num_requests=-1), 1), (dict(topk=-1), 1),
+    (dict(max_pages=0), 1), (dict(num_rows=9), 1), (dict(sm_scale=float("inf")), 1),
+])
+def test_shape_validation(kw, status):
+    sh = _shape(**kw)
+    pg = _paged()
+    assert _raw("qsa_index_scores", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, None) == status
+    assert _raw("qsa_select_topk", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, None) == status
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
+                1 << 30, None) == status
+    assert q.qsa_workspace_bytes(sh, 0) == 0
+
+
+def test_pointer_validation():
+    sh, pg = _shape(), _paged()
+    # NULL shape / paged / required tensors
+    assert _raw("qsa_index_scores", None, ctypes.byref(pg), FAKE, FAKE, None) == 1
+    assert _raw("qsa_index_scores", ctypes.byref(sh), None, FAKE, FAKE, None) == 1
+    assert _raw("qsa_index_scores", ctypes.byref(sh), ctypes.byref(pg), None, FAKE, None) == 1
+    assert _raw("qsa_select_topk", ctypes.byref(sh), ctypes.byref(pg), FAKE, None, None) == 1
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(v_codes=None)), FAKE, FAKE, FAKE,
+                None, 0, FAKE, 1 << 30, None) == 1
+    # misaligned tensors
+    assert _raw("qsa_index_scores", ctypes.byref(sh), ctypes.byref(pg), FAKE + 2, FAKE, None) == 1
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(k_codes=FAKE + 8)), FAKE, FAKE, FAKE,
+                None, 0, FAKE, 1 << 30, None) == 1
+    # negative split count, non-finite global scale
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, -1, FAKE,
+                1 << 30, None) == 1
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(k_global=float("nan"))), FAKE, FAKE,
+                FAKE, None, 0, FAKE, 1 << 30, None) == 1
+    # too many q columns per request (4 rows x 32 heads per KV head)
+    big = _shape(num_q_heads=128)
+    assert _raw("qsa_sparse_decode", ctypes.byref(big), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
+                1 << 30, None) == 2
+
+
+def test_workspace_sizing():
+    sh = _shape()
+    assert q.qsa_workspace_bytes(sh, 1) == 0
+    per = 8 * 32
+    o = 4 * per * 128 * 4
+    assert q.qsa_workspace_bytes(sh, 4) == ((o + 255) // 256) * 256 + 4 * per * 2 * 4
+    assert q.qsa_workspace_bytes(sh, 1000) == q.qsa_workspace_bytes(sh, 64)
+    # a too-small workspace is refused before any launch
+    pg = _paged()
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 4, FAKE,
+                q.qsa_workspace_bytes(sh, 4) - 1, None) == 3
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 4, None,
+                1 << 30, None) == 3
+
+
+def test_empty_batches_are_no_ops():
+    sh = _shape(num_requests=0, num_rows=0)
+    pg = _paged()
+    assert _raw("qsa_index_scores", ctypes.byref(sh), ctypes.byref(pg), None, None, None) == 0
+    assert _raw("qsa_select_topk", ctypes.byref(sh), ctypes.byref(pg), None, None, None) == 0
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), None, None, None, None, 0, None, 0,
+                None) == 0
+    dq = _shape()
+    assert _raw("qsa_nvfp4_dequant_pages", ctypes.byref(dq), None, None, ctypes.c_float(1.0), None, 0, None,
+                None) == 0
