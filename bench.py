@@ -1,0 +1,220 @@
+"""Benchmark: query-sparse NVFP4 decode / verify attention, one step = one layer's hot path.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mtp_verify_32k]
+
+A step runs the whole path over one batch on one GPU:
+index scores -> canonical top-k -> split-KV attention (with its merge).
+
+Inputs are synthetic and seeded (module `synth`), already resident in HBM. The paged
+cache is replicated over several "layers", and consecutive steps walk through them,
+as a decode step walks through a model's attention layers. So each step reads its K/V
+from HBM, not from the 256 MB MALL (the pages a step touches are evicted before that
+layer comes round again).
+
+Output: one JSON line with the contract's fields plus
+  roofline      -- the dominant kernel (qsa_sparse_decode) against MI355X's 8 TB/s HBM peak,
+                   from algorithmic bytes per launch and HIP-event durations on its stream;
+  cpu_baseline  -- the CPU oracle on a bounded sample of the same workload (single thread);
+  stages        -- mean HIP-event microseconds of each of the three calls.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse NVFP4 decode attention: µs/step + achieved HBM GB/s (% of peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+
+
+def algorithmic_bytes(w, selected):
+    """Bytes the method must move per step (the layout's minimum), from the actual selection.
+
+    attention: for each request and KV head, every distinct valid page that any of its rows
+    selected, K + V codes and scales (P * (d/2 + d/16) * 2 bytes); plus q, out, lse, the
+    selection rows and the page-table entries it reads.
+    index:     every candidate page's key for every KV head, q, and the score table written.
+    select:    the score table read and the selection written.
+    """
+    import numpy as np
+    c = w.cfg
+    P, d, Hq, Hkv = c.page_size, c.head_dim, c.q_heads, c.kv_heads
+    KW = c.topk + c.window
+    page_bytes = P * (d // 2 + d // 16) * 2          # K + V of one (page, KV head)
+    attn_kv = 0
+    pt_entries = 0
+    index_keys = 0
+    for b in range(w.B):
+        r0, r1 = int(w.row_offsets[b]), int(w.row_offsets[b + 1])
+        R = r1 - r0
+        listed = set()
+        cand = set()
+        for j in range(R):
+            for p in selected[r0 + j]:
+                if p >= 0:
+                    listed.add(int(p))
+            L = int(w.seq_lens[b]) - (R - 1 - j)
+            n = min(-(-max(L, 0) // P), w.MP)
+            for p in range(max(0, n - c.window)):
+                if w.page_table[b, p] >= 0:
+                    cand.add(p)
+        valid = [p for p in listed if w.page_table[b, p] >= 0]
+        attn_kv += len(valid) * Hkv * page_bytes
+        pt_entries += len(listed)
+        index_keys += len(cand) * Hkv * d * 2
+    qo = w.N * Hq * d * 2
+    attn = attn_kv + qo + qo + w.N * Hq * 4 + w.N * KW * 4 + pt_entries * 4
+    index = index_keys + qo + w.N * w.MP * 4
+    select = w.N * w.MP * 4 + w.N * KW * 4
+    return dict(attention=attn, attention_kv=attn_kv, index=index, select=select,
+                step=attn + index + select)
+
+
+def cpu_baseline(w, max_rows):
+    """The CPU oracle (single-threaded C) on the first rows of the batch, scaled to a step."""
+    import numpy as np
+    import oracle
+    import synth
+    # a sub-batch of whole requests
+    nb = 0
+    while nb < w.B and int(w.row_offsets[nb + 1]) <= max_rows:
+        nb += 1
+    nb = max(1, nb)
+    rows = int(w.row_offsets[nb])
+    sub = synth.Workload(w.cfg, w.page_table[:nb], w.seq_lens[:nb], w.row_offsets[:nb + 1],
+                         w.q[:rows], w.k_codes, w.k_scales, w.v_codes, w.v_scales, w.index_keys)
+    t0 = time.perf_counter()
+    s = oracle.index_scores(sub)
+    sel = oracle.select_w(sub, s)
+    oracle.attention(sub, sel)
+    dt = time.perf_counter() - t0
+    per_step_s = dt * w.N / rows
+    return per_step_s, rows, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="mtp_verify_32k")
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=32, help="rows of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for PMC byte-counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path shards by request with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synth
+    import block_sparse_decode_amd as q
+    from block_sparse_decode_amd.batch import DeviceBatch, Step
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    q.lib()
+    w = synth.generate(args.workload)
+    base = DeviceBatch.upload(w, dev)
+    # layer copies of the pools (distinct HBM addresses, same contents)
+    layers = [base]
+    for _ in range(1, args.layers):
+        b = DeviceBatch(**{**base.__dict__})
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "index_keys"):
+            setattr(b, name, getattr(base, name).clone())
+        layers.append(b)
+    steps = [Step(b, num_splits=args.splits) for b in layers]
+    stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        steps[i % len(steps)](stream)
+    torch.cuda.synchronize()
+    sel = steps[0].selected.cpu().numpy()
+    splits = args.splits if args.splits > 0 else None
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        st = steps[i % len(steps)]
+        e = ev[i]
+        e[0].record(stream)
+        st.scores_call(stream)
+        e[1].record(stream)
+        st.select_call(stream)
+        e[2].record(stream)
+        st.decode_call(stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_idx = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3     # us
+    t_sel = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e3
+    t_dec = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in ev]) * 1e3
+    err = int(base.error_word[0].item())
+
+    ab = algorithmic_bytes(w, sel)
+    us_step = wall / K * 1e6
+    dec_us = float(np.mean(t_dec))
+    achieved = ab["attention"] / (dec_us * 1e-6) / 1e9
+    step_gbs = ab["step"] / (us_step * 1e-6) / 1e9
+
+    c = w.cfg
+    out = {
+        "metric": METRIC,
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "us_per_step": round(us_step, 2),
+        "us_per_step_events": round(float(np.mean(t_step)), 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": c.name, "batch": c.batch, "rows_per_request": c.rows, "q_heads": c.q_heads,
+                   "kv_heads": c.kv_heads, "head_dim": c.head_dim, "page_size": c.page_size,
+                   "context": c.context, "topk": c.topk, "window": c.window, "kv_cache": "nvfp4",
+                   "layers_rotated": args.layers,
+                   "num_splits": splits or "auto"},
+        "stages": {"index_scores_us": round(float(np.mean(t_idx)), 2),
+                   "select_topk_us": round(float(np.mean(t_sel)), 2),
+                   "sparse_decode_us": round(dec_us, 2),
+                   "sparse_decode_us_p10": round(float(np.percentile(t_dec, 10)), 2),
+                   "sparse_decode_us_p90": round(float(np.percentile(t_dec, 90)), 2)},
+        "bytes": ab,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "qsa_sparse_decode (sparse_decode_kernel + merge_splits_kernel)"},
+        "error_word": err,
+    }
+    if args.cpu_rows > 0:
+        per_step_s, rows, dt = cpu_baseline(w, args.cpu_rows)
+        out["cpu_baseline"] = {"value": round(ab["step"] / per_step_s / 1e9, 4), "unit": "GB/s",
+                               "us_per_step": round(per_step_s * 1e6, 1), "cores": 1, "kind": "oracle",
+                               "sample": f"first {rows} of {w.N} rows (whole requests), all three stages, "
+                                         f"{dt:.1f} s single-threaded, scaled to the full step"}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
