@@ -44,23 +44,27 @@ qsa_status check_rows_ptrs(const qsa_paged *pg)
     return QSA_OK;
 }
 
+// 16-column tiles of a request's (rows x q heads per KV head) query columns
 int col_tiles(const qsa_shape *sh)
 {
     const int cols = sh->max_rows_per_request * (sh->num_q_heads / sh->num_kv_heads);
-    return cols <= 16 ? 1 : cols <= 32 ? 2 : 4;
+    return (cols + 15) / 16;
 }
 
-// Splits per (request, KV head) when the caller leaves the choice to the library: enough
-// workgroups to give each of the 256 CUs about three, without splits so thin that a wave
-// gets fewer than two pages of the expected union.
+// Splits per (request, KV head, column tile) when the caller leaves the choice to the
+// library: about one workgroup (8 waves) per CU over the 256 CUs, without splits so thin
+// that a wave gets less than one page of the expected union. (Two workgroups fit per CU;
+// fewer, longer workgroups measured faster than one full round of short ones, because each
+// workgroup pays the union build and each split adds partials to merge.)
 int auto_splits(const qsa_shape *sh)
 {
-    const int64_t base = (int64_t)sh->num_requests * sh->num_kv_heads;
+    const int64_t base = (int64_t)sh->num_requests * sh->num_kv_heads * col_tiles(sh);
     if (base <= 0) return 1;
-    const int64_t union_est = std::min<int64_t>((int64_t)sh->max_rows_per_request * (sh->topk + sh->window),
-                                                sh->max_pages);
-    int64_t s = (768 + base - 1) / base;
-    const int64_t cap = std::max<int64_t>(1, union_est / (2 * kDecodeWaves));
+    const int G = sh->num_q_heads / sh->num_kv_heads;
+    const int64_t rows_per_tile = std::max<int64_t>(1, std::min<int64_t>(sh->max_rows_per_request, (16 + G - 1) / G));
+    const int64_t union_est = std::min<int64_t>(rows_per_tile * (sh->topk + sh->window), sh->max_pages);
+    int64_t s = (256 + base - 1) / base;
+    const int64_t cap = std::max<int64_t>(1, union_est / kDecodeWaves);
     s = std::min(s, cap);
     s = std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits));
     return (int)s;
@@ -121,6 +125,7 @@ qsa_status qsa_index_scores(const qsa_shape *sh, const qsa_paged *pg, const uint
     prm.N = sh->num_rows;
     prm.MP = sh->max_pages;
     prm.P = sh->page_size;
+    prm.log2P = sh->page_size == 64 ? 6 : 7;
     prm.W = sh->window;
     prm.Hq = sh->num_q_heads;
     prm.Hkv = sh->num_kv_heads;
@@ -147,6 +152,7 @@ qsa_status qsa_select_topk(const qsa_shape *sh, const qsa_paged *pg, const float
     prm.N = sh->num_rows;
     prm.MP = sh->max_pages;
     prm.P = sh->page_size;
+    prm.log2P = sh->page_size == 64 ? 6 : 7;
     prm.k = sh->topk;
     prm.W = sh->window;
     prm.rmax = sh->max_rows_per_request;
@@ -209,14 +215,16 @@ qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uin
     prm.N = sh->num_rows;
     prm.MP = sh->max_pages;
     prm.P = sh->page_size;
+    prm.log2P = sh->page_size == 64 ? 6 : 7;
     prm.KW = sh->topk + sh->window;
     prm.Hq = sh->num_q_heads;
     prm.Hkv = sh->num_kv_heads;
     prm.rmax = sh->max_rows_per_request;
     prm.splits = splits;
+    prm.col_tiles = col_tiles(sh);
     prm.qk_scale_log2 = (float)((double)sh->sm_scale * (double)pg->k_global * 1.4426950408889634);
     prm.v_global = pg->v_global;
-    hipError_t e = launch_sparse_decode(prm, sh->head_dim, sh->num_requests, col_tiles(sh), (hipStream_t)stream);
+    hipError_t e = launch_sparse_decode(prm, sh->head_dim, sh->num_requests, (hipStream_t)stream);
     return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
 }
 

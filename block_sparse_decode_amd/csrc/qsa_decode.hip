@@ -78,64 +78,141 @@ __device__ __forceinline__ uint32_t raw_dword(const RawTile<D> &t, int i)
     }
 }
 
-// Dequantise a lane's 8-element group i (elements 8i..8i+7 of its d/4 chunk).
+// Dequantise a lane's 8-element group i (elements 8i..8i+7 of its d/4 chunk); `sc` holds
+// the chunk's block scales as f16 ({s0, s1} for d = 128, {s0, -} for d = 64).
 template <int D>
-__device__ __forceinline__ f16x8 dequant_group(const RawTile<D> &t, int i)
+__device__ __forceinline__ f16x8 dequant_group(const RawTile<D> &t, f16x2 sc, int i)
 {
-    const uint32_t sb = (D == 128 && i >= 2) ? (t.scales >> 8) & 0xffu : t.scales & 0xffu;
-    return nvfp4_dequant8(raw_dword<D>(t, i), e4m3_to_f16(sb));
+    return nvfp4_dequant8(raw_dword<D>(t, i), (D == 128 && i >= 2) ? sc.y : sc.x);
 }
 
-template <int D, int NCT>
-__global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_kernel(DecodeParams prm)
+template <int D>
+__device__ __forceinline__ void load_unit(const DecodeParams &prm, int phys, int g, int c, int li, int gq,
+                                          RawTile<D> (&kr)[2], RawTile<D> (&vr)[2])
+{
+    const int64_t head = (int64_t)phys * prm.Hkv + g;
+    const int64_t tok = head * prm.P + c * 32 + li;                 // token index in the pool
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int64_t t = tok + mt * 16;
+        kr[mt] = load_raw<D>(prm.k_codes + t * (D / 2), prm.k_scales + t * (D / 16), gq);
+        vr[mt] = load_raw<D>(prm.v_codes + t * (D / 2), prm.v_scales + t * (D / 16), gq);
+    }
+}
+
+// V staging in LDS: row t (token) holds D f16 values as D/8 chunks of 16 bytes; chunk ch of
+// row t is stored at chunk position ch ^ swz(t). With swz(t) = (2t + t/8) mod 16 (a
+// permutation of 0..15), the 16 lanes writing one chunk of 16 consecutive rows hit 16
+// different bank groups, and the transposed reads (4 rows x 2 chunks per 16 lanes) do too.
+__device__ __forceinline__ int vswz(int row) { return ((row << 1) + ((row >> 3) & 1)) & 15; }
+
+// Position in a wave's list of 32-token sub-chunks (entry e of the union, sub-chunk c).
+struct UnitCursor {
+    int e, c;
+    uint32_t pm;
+    int phys;
+    bool have;
+};
+
+__device__ __forceinline__ UnitCursor first_unit(int e, int e_hi, const uint32_t *u_pm, const int32_t *u_phys)
+{
+    UnitCursor u;
+    u.e = e;
+    u.c = 0;
+    u.have = e < e_hi;
+    u.pm = u.have ? __builtin_amdgcn_readfirstlane(u_pm[e]) : 0u;
+    u.phys = u.have ? __builtin_amdgcn_readfirstlane(u_phys[e]) : 0;
+    return u;
+}
+
+__device__ __forceinline__ UnitCursor next_unit(UnitCursor u, int stride, int e_hi, const uint32_t *u_pm,
+                                                const int32_t *u_phys)
+{
+    if (!u.have) return u;
+    if (u.c + 1 < (int)(u.pm >> 24)) {
+        u.c += 1;
+        return u;
+    }
+    return first_unit(u.e + stride, e_hi, u_pm, u_phys);
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(DecodeParams prm)
 {
     constexpr int NW = kDecodeWaves;
     constexpr int NT = NW * 64;
-    constexpr int VROW = D + 16;            // padded LDS row of one V token (f16)
     constexpr int KS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int DQ = D / 4;               // elements per lane group
     constexpr int NDT = D / 16;             // 16-row d tiles of O^T
-    constexpr int NCOL = NCT * 16;
-    static_assert(NCOL * D * 4 <= NW * 32 * VROW * 2, "merge buffer must fit the V staging area");
+    // A column's running max is raised only when a logit exceeds it by more than this
+    // (log2 units), so most sub-chunks skip the rescale; P stays <= 2^8 in f16.
+    constexpr float kLazy = 8.0f;
+    static_assert((NW / 2) * (NDT + 1) * 64 * 16 <= NW * 32 * D * 2, "merge slots must fit the V staging area");
+    static_assert(D / 8 <= 16, "one V row holds at most 16 swizzled chunks");
 
-    __shared__ __attribute__((aligned(16))) half_t vsm[NW][32 * VROW];
-    __shared__ uint32_t u_pm[kMaxUnion];    // page | row mask << 16
+    __shared__ __attribute__((aligned(16))) half_t vsm[NW][32 * D];
+    __shared__ uint32_t u_pm[kMaxUnion];    // page | row mask << 16 | sub-chunks << 24
     __shared__ int32_t u_phys[kMaxUnion];
-    __shared__ float ml_m[NW][NCOL];
-    __shared__ float ml_l[NW][NCOL];
+    __shared__ float ml_m[NW][16];
     __shared__ uint32_t scan_tmp[NT / 64 + 1];
+    __shared__ f16x8 q_lds[KS][64];         // the tile's q operand, in MFMA B-operand lane order
 
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int s = blockIdx.x, b = blockIdx.z;
+    const int T = prm.col_tiles;
+    const int g = blockIdx.y / T, ct = blockIdx.y - g * T;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int gq = lane >> 4, li = lane & 15;
     const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
-    const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, tid == 0 && s == 0 && g == 0);
+    const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, tid == 0 && s == 0 && blockIdx.y == 0);
     const int Rb = r1 - r0;         // the request's own row count fixes each row's length
-    if (R <= 0) return;
     const int G = prm.Hq / prm.Hkv;
+    const int col0 = ct * 16;       // this tile: columns col0..col0+15 of the request's R x G
+    if (col0 >= R * G) return;
+    const int j_lo = col0 / G;
+    const int j_hi = min(R - 1, (col0 + 15) / G);
+    const int nrow = j_hi - j_lo + 1;                // rows of this tile (<= 4)
     const int MP = prm.MP, P = prm.P, KW = prm.KW;
     const int64_t Lb = prm.seq_lens[b];
 
-    // ---- 1. union of the rows' selected pages --------------------------------------
+    // ---- 1. union of the tile's rows' selected pages --------------------------------
+    // LDS scratch in the V staging area: this request's page-table row and a row-mask
+    // bitmap (one byte per page). Both the page-table row and the selection rows are read
+    // right away, so the union costs one dependent global round trip.
+    const int nwords = ((MP + 3) / 4 + 3) & ~3;
     uint32_t *bm = reinterpret_cast<uint32_t *>(&vsm[0][0]);
-    const int nwords = (MP + 3) / 4;
+    int32_t *pt_row = reinterpret_cast<int32_t *>(bm + nwords);
     for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
+    for (int p = tid; p < MP; p += NT) pt_row[p] = prm.page_table[(int64_t)b * MP + p];
+    constexpr int kSelPerThread = (kMaxUnion + NT - 1) / NT;
+    int selp[kSelPerThread];
+#pragma unroll
+    for (int i = 0; i < kSelPerThread; ++i) {
+        const int idx = tid + i * NT;
+        selp[i] = -1;
+        if (idx < nrow * KW) {
+            const int jr = idx / KW, e = idx - jr * KW;
+            selp[i] = prm.selected[(int64_t)(r0 + j_lo + jr) * KW + e];
+        }
+    }
     __syncthreads();
-    for (int idx = tid; idx < R * KW; idx += NT) {
-        const int j = idx / KW, e = idx - j * KW;
-        const int p = prm.selected[(int64_t)(r0 + j) * KW + e];
+#pragma unroll
+    for (int i = 0; i < kSelPerThread; ++i) {
+        const int idx = tid + i * NT;
+        if (idx >= nrow * KW) break;
+        const int jr = idx / KW;
+        const int p = selp[i];
         if (p < -1 || p >= MP) {
             set_error(prm.err, QSA_DEVERR_SELECTED);
             continue;
         }
-        if (p < 0 || p >= row_geom(Lb, Rb, j, P, MP).pages) continue;   // no visible token
-        const int phys = prm.page_table[(int64_t)b * MP + p];
+        if (p < 0 || p >= row_geom(Lb, Rb, j_lo + jr, prm.log2P, MP).pages) continue;   // no visible token
+        const int phys = pt_row[p];
         if (phys == -1) continue;
         if (phys < -1 || (int64_t)phys >= prm.NP) {
             set_error(prm.err, QSA_DEVERR_PAGE_ID);
             continue;
         }
-        atomicOr(&bm[p >> 2], 1u << ((p & 3) * 8 + j));
+        atomicOr(&bm[p >> 2], 1u << ((p & 3) * 8 + jr));
     }
     __syncthreads();
     uint32_t U;
@@ -149,254 +226,215 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void sparse_decode_kernel(Decode
         uint32_t pos = block_exclusive_scan<NT>(cnt, scan_tmp, &U);
         for (int w = tid * CW; w < (tid + 1) * CW && w < nwords; ++w) {
             const uint32_t x = bm[w];
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t m = (x >> (8 * q)) & 0xffu;
-                if (m) u_pm[pos++] = (uint32_t)(4 * w + q) | (m << 16);
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const uint32_t m = (x >> (8 * q4)) & 0xffu;
+                if (!m) continue;
+                const int p = 4 * w + q4;
+                // sub-chunks of 32 tokens that the longest requesting row can see
+                const int jmax = j_lo + 31 - __builtin_clz(m);     // later rows see more tokens
+                const int64_t vis = row_geom(Lb, Rb, jmax, prm.log2P, MP).len - ((int64_t)p << prm.log2P);
+                const int nc = (int)(vis >= P ? P / 32 : (vis + 31) / 32);
+                u_pm[pos] = (uint32_t)p | (m << 16) | ((uint32_t)nc << 24);
+                u_phys[pos] = pt_row[p];
+                ++pos;
             }
         }
     }
-    __syncthreads();
-    for (int e = tid; e < (int)U; e += NT) u_phys[e] = prm.page_table[(int64_t)b * MP + (u_pm[e] & 0xffffu)];
 
-    // ---- 2. q operand and per-column bookkeeping ------------------------------------
-    f16x8 qop[NCT][KS];
-    int jcol[NCT];                  // row of this lane's column (R = padding column)
-    uint32_t tile_rows[NCT];        // rows that a column tile touches
+    // ---- 2. q operand of this lane's column --------------------------------------
+    const int col = col0 + li;
+    const int jc = col / G;                           // row of this lane's column
+    const bool colv = jc < R;                         // false: padding column
+    const int jbit = colv ? jc - j_lo : 31;           // its bit in a page's row mask
+    const int64_t lcol = colv ? row_geom(Lb, Rb, jc, prm.log2P, MP).len : 0;
     bool qbad = false;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int col = ct * 16 + li;
-        const int j = col / G;
-        jcol[ct] = j < R ? j : R;
-        uint32_t rows = 0;
-        for (int jj = 0; jj < R; ++jj)
-            if (jj * G < (ct + 1) * 16 && (jj + 1) * G > ct * 16) rows |= 1u << jj;
-        tile_rows[ct] = rows;
+    if (wave == 0) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             f16x8 v = {};
-            if (j < R) {
-                const int h = g * G + (col - j * G);
+            if (colv) {
+                const int h = g * G + (col - jc * G);
                 const uint4 raw = *reinterpret_cast<const uint4 *>(
-                    prm.q + ((int64_t)(r0 + j) * prm.Hq + h) * D + gq * DQ + ks * 8);
-                const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+                    prm.q + ((int64_t)(r0 + jc) * prm.Hq + h) * D + gq * DQ + ks * 8);
+                const float f[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
+                                    bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float lo = bf16lo(w4[t]), hi = bf16hi(w4[t]);
-                    qbad |= !(fabsf(lo) <= 65504.0f) || !(fabsf(hi) <= 65504.0f);
-                    v[2 * t] = (half_t)lo;
-                    v[2 * t + 1] = (half_t)hi;
-                }
+                for (int t = 0; t < 8; ++t) qbad |= !(fabsf(f[t]) <= 65504.0f);
+                const f16x2 h0 = {(half_t)f[0], (half_t)f[1]}, h1 = {(half_t)f[2], (half_t)f[3]};
+                const f16x2 h2 = {(half_t)f[4], (half_t)f[5]}, h3 = {(half_t)f[6], (half_t)f[7]};
+                v = __builtin_shufflevector(__builtin_shufflevector(h0, h1, 0, 1, 2, 3),
+                                            __builtin_shufflevector(h2, h3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            qop[ct][ks] = v;
+            q_lds[ks][lane] = v;
         }
     }
     if (qbad) set_error(prm.err, QSA_DEVERR_Q_RANGE);
-    __syncthreads();                 // u_phys ready; the bitmap area becomes V staging
+    __syncthreads();                 // union list ready; the scratch area becomes V staging
 
-    // ---- 3. online softmax over this wave's pages ---------------------------------
+    // ---- 3. online softmax over this wave's sub-chunks, the next one in flight -----
     const int S = prm.splits;
-    const int e_lo = (int)(((int64_t)s * U) / S), e_hi = (int)(((int64_t)(s + 1) * U) / S);
+    const int e_lo = (s * (int)U) / S, e_hi = ((s + 1) * (int)U) / S;
     const float c1 = prm.qk_scale_log2;
     const float NEG_INF = -__builtin_inff();
 
-    f32x4 oacc[NCT][NDT];
-    float m_run[NCT], l_run[NCT];
+    // O^T accumulators; tile NDT is a ones-row of V, so it accumulates sum_t P[t][col],
+    // the softmax denominator of the very f16 P values that feed the other tiles.
+    f32x4 oacc[NDT + 1];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        m_run[ct] = NEG_INF;
-        l_run[ct] = 0.0f;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) oacc[ct][dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
+    for (int dt = 0; dt <= NDT; ++dt) oacc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m_col = NEG_INF;
     half_t *vs = &vsm[wave][0];
-    const int64_t head_stride = (int64_t)P * (D / 2);       // codes bytes of one (page, KV head)
-    const int64_t sc_stride = (int64_t)P * (D / 16);
+    const f16x8 ones = {(half_t)1.0f, (half_t)1.0f, (half_t)1.0f, (half_t)1.0f,
+                        (half_t)1.0f, (half_t)1.0f, (half_t)1.0f, (half_t)1.0f};
+    const int trow = 4 * gq + (li >> 2);            // transposed-read rows trow, trow + 16
 
-    for (int e = e_lo + wave; e < e_hi; e += NW) {
-        const uint32_t pm = __builtin_amdgcn_readfirstlane(u_pm[e]);
-        const int phys = __builtin_amdgcn_readfirstlane(u_phys[e]);
-        const int p = (int)(pm & 0xffffu);
-        const uint32_t rmask = pm >> 16;
-        const uint8_t *kc_page = prm.k_codes + ((int64_t)phys * prm.Hkv + g) * head_stride;
-        const uint8_t *ks_page = prm.k_scales + ((int64_t)phys * prm.Hkv + g) * sc_stride;
-        const uint8_t *vc_page = prm.v_codes + ((int64_t)phys * prm.Hkv + g) * head_stride;
-        const uint8_t *vsc_page = prm.v_scales + ((int64_t)phys * prm.Hkv + g) * sc_stride;
+    // One register set: a sub-chunk's raw codes are consumed (K into the MFMA operands, V into
+    // LDS) before the next sub-chunk's loads are issued into the same registers; those loads
+    // are then in flight during the softmax and the P.V products.
+    RawTile<D> kr[2], vr[2];
+    auto process = [&](const UnitCursor &u, const UnitCursor &un) {
+        const int p = (int)(u.pm & 0xffffu);
+        const uint32_t rmask = (u.pm >> 16) & 0xffu;
+        const int64_t tok0 = ((int64_t)p << prm.log2P) + u.c * 32;
 
-        for (int c = 0; c < P / 32; ++c) {
-            const int64_t tok0 = (int64_t)p * P + c * 32;
-            // longest row of this page decides whether the sub-chunk has any visible token
-            int64_t lmax = 0;
-            for (int jj = 0; jj < R; ++jj)
-                if ((rmask >> jj) & 1u) {
-                    const int64_t L = row_geom(Lb, Rb, jj, P, MP).len;
-                    lmax = L > lmax ? L : lmax;
-                }
-            if (lmax <= tok0) break;
-
-            RawTile<D> kr[2], vr[2];
+        // S^T = K Q^T (unscaled logits)
+        f32x4 sacc[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int t = c * 32 + mt * 16 + li;
-                kr[mt] = load_raw<D>(kc_page + (int64_t)t * (D / 2), ks_page + (int64_t)t * (D / 16), gq);
-                vr[mt] = load_raw<D>(vc_page + (int64_t)t * (D / 2), vsc_page + (int64_t)t * (D / 16), gq);
-            }
-
-            bool act[NCT];
+        for (int mt = 0; mt < 2; ++mt) {
+            const f16x2 ksc = e4m3x2_to_f16x2(kr[mt].scales);
+            sacc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) act[ct] = (rmask & tile_rows[ct]) != 0u;
-
-            // S^T = K Q^T
-            f32x4 sacc[2][NCT];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) sacc[mt][ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const f16x8 a = dequant_group<D>(kr[mt], ks);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-                        if (act[ct])
-                            sacc[mt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qop[ct][ks], sacc[mt][ct], 0, 0, 0);
-                }
-            }
-
-            // V -> LDS, token-major rows of this 32-token sub-chunk
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                for (int i = 0; i < DQ / 8; ++i) {
-                    const f16x8 v = dequant_group<D>(vr[mt], i);
-                    *reinterpret_cast<f16x8 *>(vs + (mt * 16 + li) * VROW + gq * DQ + i * 8) = v;
-                }
-            }
-            wave_lds_fence();
-
-            // online softmax; P stays in registers as the B operand of O^T += V^T P^T
-            f16x8 pop[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                if (!act[ct]) continue;
-                int lim = 0;
-                const int j = jcol[ct];
-                if (j < R && ((rmask >> j) & 1u)) {
-                    const int64_t vis = row_geom(Lb, Rb, j, P, MP).len - tok0;
-                    lim = vis <= 0 ? 0 : (vis >= 32 ? 32 : (int)vis);
-                }
-                float x[8];
-                float mloc = NEG_INF;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int t = mt * 16 + gq * 4 + r;
-                        const float v = (t < lim) ? sacc[mt][ct][r] * c1 : NEG_INF;
-                        x[mt * 4 + r] = v;
-                        mloc = fmaxf(mloc, v);
-                    }
-                mloc = max_across_groups(mloc);
-                const float m_new = fmaxf(m_run[ct], mloc);
-                const bool none = (m_new == NEG_INF);
-                const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m_run[ct] - m_new);
-                float psum = 0.0f;
-                f16x8 pv;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float pr = none ? 0.0f : __builtin_amdgcn_exp2f(x[i] - m_new);
-                    psum += pr;
-                    pv[i] = (half_t)pr;
-                }
-                pop[ct] = pv;
-                l_run[ct] = l_run[ct] * alpha + psum;
-                m_run[ct] = m_new;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) oacc[ct][dt] *= alpha;
-            }
-
-            // O^T += V^T P^T
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const half_t *a0 = vs + (4 * gq + (li >> 2)) * VROW + dt * 16 + 4 * (li & 3);
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a0));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a0 + 16 * VROW));
-                const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    if (act[ct])
-                        oacc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop[ct], oacc[ct][dt], 0, 0, 0);
-            }
-            wave_lds_fence();
+            for (int ks = 0; ks < KS; ++ks)
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_group<D>(kr[mt], ksc, ks), q_lds[ks][lane],
+                                                                  sacc[mt], 0, 0, 0);
         }
+
+        // V -> LDS, token-major rows of this 32-token sub-chunk (16-byte chunks swizzled)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const f16x2 vsc = e4m3x2_to_f16x2(vr[mt].scales);
+            const int row = mt * 16 + li;
+#pragma unroll
+            for (int i = 0; i < DQ / 8; ++i) {
+                const int ch = gq * (DQ / 8) + i;
+                *reinterpret_cast<f16x8 *>(vs + row * D + ((ch ^ vswz(row)) & (D / 8 - 1)) * 8) =
+                    dequant_group<D>(vr[mt], vsc, i);
+            }
+        }
+        if (un.have) load_unit<D>(prm, un.phys, g, un.c, li, gq, kr, vr);
+
+        // online softmax with a lazily raised column max; P stays in registers
+        int lim = 0;
+        if ((rmask >> jbit) & 1u) {
+            const int64_t vis = lcol - tok0;
+            lim = vis <= 0 ? 0 : (vis >= 32 ? 32 : (int)vis);
+        }
+        float x[8];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[mt * 4 + r] = sacc[mt][r];
+        if (__any(lim > 0 && lim < 32)) {
+            // a row ends inside this sub-chunk: mask token by token
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((i / 4) * 16 + gq * 4 + (i & 3) >= lim) x[i] = NEG_INF;
+        } else if (__any(lim == 0)) {
+            // whole columns are masked (their row did not select this page, or padding)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = lim ? x[i] : NEG_INF;
+        }
+        const float lmx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        if (__any(lmx * c1 > m_col + kLazy)) {
+            const float m_new = fmaxf(m_col, max_across_groups(lmx) * c1);
+            const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(m_col - m_new);
+#pragma unroll
+            for (int dt = 0; dt <= NDT; ++dt) oacc[dt] *= alpha;
+            m_col = m_new;
+        }
+        const float negm = (m_col == NEG_INF) ? NEG_INF : -m_col;
+        float pr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c1, negm));
+        const f16x2 p0 = {(half_t)pr[0], (half_t)pr[1]}, p1 = {(half_t)pr[2], (half_t)pr[3]};
+        const f16x2 p2 = {(half_t)pr[4], (half_t)pr[5]}, p3 = {(half_t)pr[6], (half_t)pr[7]};
+        const f16x8 pop = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                                  __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+
+        // O^T += V^T P^T, and the ones-row tile for the denominator
+        wave_lds_fence();            // this wave's V staging writes are complete
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int ch = 2 * dt + ((li >> 1) & 1), sub = (li & 1) * 4;
+            const half_t *a0 = vs + trow * D + ((ch ^ vswz(trow)) & (D / 8 - 1)) * 8 + sub;
+            const half_t *a1 = vs + (trow + 16) * D + ((ch ^ vswz(trow + 16)) & (D / 8 - 1)) * 8 + sub;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a0));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a1));
+            const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pop, oacc[dt], 0, 0, 0);
+        }
+        oacc[NDT] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop, oacc[NDT], 0, 0, 0);
+    };
+
+    UnitCursor u = first_unit(e_lo + wave, e_hi, u_pm, u_phys);
+    if (u.have) load_unit<D>(prm, u.phys, g, u.c, li, gq, kr, vr);
+    while (u.have) {
+        const UnitCursor un = next_unit(u, NW, e_hi, u_pm, u_phys);
+        process(u, un);
+        u = un;
     }
 
-    // ---- 4. merge the waves (fixed order), then write ------------------------------
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const float lt = sum_across_groups(l_run[ct]);
-        if (gq == 0) {
-            ml_m[wave][ct * 16 + li] = m_run[ct];
-            ml_l[wave][ct * 16 + li] = lt;
-        }
-    }
-    __syncthreads();
-    float wgt[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int col = ct * 16 + li;
+    // ---- 4. merge the waves in LDS (fixed tree order), then write ------------------
+    if (gq == 0) ml_m[wave][li] = m_col;
+    __syncthreads();                 // all waves are done with their V staging
+    {
         float M = NEG_INF;
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_m[w][col]);
-        wgt[ct] = (M == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(m_run[ct] - M);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_m[w][li]);
+        const float wgt = (M == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(m_col - M);
+#pragma unroll
+        for (int dt = 0; dt <= NDT; ++dt) oacc[dt] *= wgt;
+        m_col = M;                   // common reference max of the column
     }
-    float *obuf = reinterpret_cast<float *>(&vsm[0][0]);    // [NCOL][D]
-    for (int w = 0; w < NW; ++w) {
-        if (wave == w) {
+    // slot layout [slot][dt][lane] f32x4: every lane moves 16 contiguous bytes
+    f32x4 *slots = reinterpret_cast<f32x4 *>(&vsm[0][0]);
+    constexpr int kSlot = (NDT + 1) * 64;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+    for (int half = NW / 2; half >= 1; half /= 2) {
+        if (wave >= half && wave < 2 * half) {
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
+            for (int dt = 0; dt <= NDT; ++dt) slots[(wave - half) * kSlot + dt * 64 + lane] = oacc[dt];
+        }
+        __syncthreads();
+        if (wave < half) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int col = ct * 16 + li, d = dt * 16 + gq * 4 + r;
-                        const float v = oacc[ct][dt][r] * wgt[ct];
-                        float *dst = obuf + col * D + d;
-                        *dst = (w == 0) ? v : *dst + v;
-                    }
+            for (int dt = 0; dt <= NDT; ++dt) oacc[dt] += slots[wave * kSlot + dt * 64 + lane];
         }
         __syncthreads();
     }
-    const int ncols = R * G < NCOL ? R * G : NCOL;
-    for (int idx = tid; idx < ncols * (D / 4); idx += NT) {
-        const int col = idx / (D / 4), d4 = idx - col * (D / 4);
-        const int j = col / G, hh = col - j * G;
-        const int row = r0 + j, head = g * G + hh;
-        float M = NEG_INF;
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_m[w][col]);
-        float L = 0.0f;
-        if (M != NEG_INF)
-            for (int w = 0; w < NW; ++w) L += ml_l[w][col] * __builtin_amdgcn_exp2f(ml_m[w][col] - M);
-        const f32x4 o = *reinterpret_cast<const f32x4 *>(obuf + col * D + 4 * d4);
-        if (S == 1) {
+    if (wave != 0 || !colv) return;
+    const int row = r0 + jc, head = g * G + (col - jc * G);
+    const float L = oacc[NDT][0];
+    if (S == 1) {
+        const float sc = (L > 0.0f) ? prm.v_global / L : 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const f32x4 o = oacc[dt] * sc;
             uint2 packed;
-            float lse_v;
-            if (L > 0.0f) {
-                const float sc = prm.v_global / L;
-                packed.x = (uint32_t)f32_to_bf16_rne(o[0] * sc) | ((uint32_t)f32_to_bf16_rne(o[1] * sc) << 16);
-                packed.y = (uint32_t)f32_to_bf16_rne(o[2] * sc) | ((uint32_t)f32_to_bf16_rne(o[3] * sc) << 16);
-                lse_v = (M + __log2f(L)) * 0.69314718055994531f;
-            } else {
-                packed.x = packed.y = 0u;
-                lse_v = NEG_INF;
-            }
-            *reinterpret_cast<uint2 *>(prm.out + ((int64_t)row * prm.Hq + head) * D + 4 * d4) = packed;
-            if (d4 == 0 && prm.lse) prm.lse[(int64_t)row * prm.Hq + head] = lse_v;
-        } else {
-            const int64_t slot = ((int64_t)s * prm.N + row) * prm.Hq + head;
-            *reinterpret_cast<f32x4 *>(prm.part_o + slot * D + 4 * d4) = o;
-            if (d4 == 0) {
-                prm.part_ml[slot * 2] = M;
-                prm.part_ml[slot * 2 + 1] = L;
-            }
+            packed.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+            packed.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+            *reinterpret_cast<uint2 *>(prm.out + ((int64_t)row * prm.Hq + head) * D + dt * 16 + gq * 4) = packed;
+        }
+        if (gq == 0 && prm.lse)
+            prm.lse[(int64_t)row * prm.Hq + head] = (L > 0.0f) ? (m_col + __log2f(L)) * 0.69314718055994531f : NEG_INF;
+    } else {
+        const int64_t slot = ((int64_t)s * prm.N + row) * prm.Hq + head;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            *reinterpret_cast<f32x4 *>(prm.part_o + slot * D + dt * 16 + gq * 4) = oacc[dt];
+        if (gq == 0) {
+            prm.part_ml[slot * 2] = m_col;
+            prm.part_ml[slot * 2 + 1] = L;
         }
     }
 }
@@ -441,15 +479,10 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams prm)
 }
 
 template <int D>
-static hipError_t launch_decode_d(const DecodeParams &prm, int B, int nct, hipStream_t stream)
+static hipError_t launch_decode_d(const DecodeParams &prm, int B, hipStream_t stream)
 {
-    dim3 grid(prm.splits, prm.Hkv, B);
-    const int nt = kDecodeWaves * 64;
-    switch (nct) {
-    case 1: sparse_decode_kernel<D, 1><<<grid, nt, 0, stream>>>(prm); break;
-    case 2: sparse_decode_kernel<D, 2><<<grid, nt, 0, stream>>>(prm); break;
-    default: sparse_decode_kernel<D, 4><<<grid, nt, 0, stream>>>(prm); break;
-    }
+    dim3 grid(prm.splits, prm.Hkv * prm.col_tiles, B);
+    sparse_decode_kernel<D><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || prm.splits == 1) return e;
     const int64_t total = (int64_t)prm.N * prm.Hq * (D / 4);
@@ -457,10 +490,9 @@ static hipError_t launch_decode_d(const DecodeParams &prm, int B, int nct, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_decode(const DecodeParams &prm, int D, int B, int ncol_tiles, hipStream_t stream)
+hipError_t launch_sparse_decode(const DecodeParams &prm, int D, int B, hipStream_t stream)
 {
-    return D == 64 ? launch_decode_d<64>(prm, B, ncol_tiles, stream)
-                   : launch_decode_d<128>(prm, B, ncol_tiles, stream);
+    return D == 64 ? launch_decode_d<64>(prm, B, stream) : launch_decode_d<128>(prm, B, stream);
 }
 
 // ---- parity hook: whole pages through the same decode as the attention kernel ----------
@@ -485,7 +517,7 @@ __global__ __launch_bounds__(256) void dequant_pages_kernel(DequantParams prm)
     const int64_t base = (int64_t)phys * prm.Hkv * prm.P + tok;   // token index in the pool
     const uint32_t codes = *reinterpret_cast<const uint32_t *>(prm.codes + base * (D / 2) + grp * 4);
     const uint32_t sb = prm.scales[base * (D / 16) + grp / 2];
-    const f16x8 v = nvfp4_dequant8(codes, e4m3_to_f16(sb));
+    const f16x8 v = nvfp4_dequant8(codes, e4m3x2_to_f16x2(sb).x);
     for (int i = 0; i < 8; ++i) dst[i] = (float)v[i] * prm.global;
 }
 

@@ -35,18 +35,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
-// E4M3FN scale byte -> f16. gfx950's fp8 convert decodes the OCP E4M3FN format
-// (all 256 codes, NaN included). Every E4M3FN value, from the 2^-9 subnormal up to 448,
-// is exact in f16, so the second conversion is exact too.
-__device__ __forceinline__ half_t e4m3_to_f16(uint32_t byte)
+// Two E4M3FN scale bytes (the low two bytes of `bytes`) -> two f16 values, exactly.
+// gfx950's scaled fp8 convert applies only its scale operand's exponent, so with scale 1.0
+// it is a plain OCP E4M3FN decode (NaN included). Every E4M3FN value, from the 2^-9
+// subnormal up to 448, is exact in f16.
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t bytes)
 {
-    float f = __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
-    return (half_t)f;
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 1.0f, false);
 }
 
 // Eight e2m1 codes (one dword; element 2i in the low nibble of byte i) times one e4m3
-// block scale -> eight f16 values, exactly.
-// The hardware fp4 convert takes its scale operand's exponent only, so it runs with
+// block scale `s` (already in f16) -> eight f16 values, exactly.
+// The hardware fp4 convert also takes its scale operand's exponent only, so it runs with
 // scale 1.0 and returns the exact e2m1 values. The block scale is then one packed f16
 // multiply per pair. An e2m1 value (<= 2 significant bits) times an e4m3 value
 // (<= 4 bits) needs at most 6 bits and lies in [2^-10, 2688], so the product is exact
@@ -58,7 +58,8 @@ __device__ __forceinline__ f16x8 nvfp4_dequant8(uint32_t codes, half_t s)
     f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
     f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
     f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
-    return (f16x8){a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+    return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3),
+                                   __builtin_shufflevector(c, d, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key), with -0 == +0.
@@ -75,18 +76,19 @@ __device__ __forceinline__ void set_error(uint32_t *err, uint32_t bit)
 }
 
 // Row geometry of an MTP verify batch: row j of a request with R rows and L_b tokens
-// sees L_b - (R - 1 - j) tokens (clipped at 0) and ceil(L / P) pages (clipped at MP).
+// sees L_b - (R - 1 - j) tokens (clipped at 0) and ceil(L / P) pages (clipped at MP);
+// P = 2^log2P.
 struct RowGeom {
     int64_t len;
     int pages;
 };
 
-__device__ __forceinline__ RowGeom row_geom(int64_t seq_len, int R, int j, int P, int MP)
+__device__ __forceinline__ RowGeom row_geom(int64_t seq_len, int R, int j, int log2P, int MP)
 {
     RowGeom g;
     int64_t L = seq_len - (int64_t)(R - 1 - j);
     if (L < 0) L = 0;
-    int64_t n = (L + P - 1) / P;
+    const int64_t n = (L + (1 << log2P) - 1) >> log2P;
     g.len = L;
     g.pages = (int)(n < MP ? n : MP);
     return g;

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void index_scores_kernel(IndexParams prm)
     }
     if (j >= R) return;
     const int row = r0 + j;
-    const RowGeom geo = row_geom(prm.seq_lens[b], r1 - r0, j, prm.P, prm.MP);
+    const RowGeom geo = row_geom(prm.seq_lens[b], r1 - r0, j, prm.log2P, prm.MP);
 
     const int p = tile * kWave + lane;
     int phys = -1;

@@ -17,7 +17,7 @@ struct IndexParams {
     float *scores;
     uint32_t *err;
     int64_t NP;
-    int N, MP, P, W, Hq, Hkv, rmax;
+    int N, MP, P, log2P, W, Hq, Hkv, rmax;
     float sm_scale;
 };
 
@@ -27,7 +27,7 @@ struct SelectParams {
     const float *scores;
     int32_t *selected;
     uint32_t *err;
-    int N, MP, P, k, W, rmax;
+    int N, MP, P, log2P, k, W, rmax;
 };
 
 struct DecodeParams {
@@ -46,7 +46,7 @@ struct DecodeParams {
     float *part_ml;           // [S][N][Hq][2] (max in log2 units, sum)
     uint32_t *err;
     int64_t NP;
-    int N, MP, P, KW, Hq, Hkv, rmax, splits;
+    int N, MP, P, log2P, KW, Hq, Hkv, rmax, splits, col_tiles;
     float qk_scale_log2;      // sm_scale * k_global * log2(e)
     float v_global;
 };
@@ -63,10 +63,10 @@ struct DequantParams {
 
 hipError_t launch_index_scores(const IndexParams &prm, int D, int B, hipStream_t stream);
 hipError_t launch_select_topk(const SelectParams &prm, int B, hipStream_t stream);
-hipError_t launch_sparse_decode(const DecodeParams &prm, int D, int B, int ncol_tiles, hipStream_t stream);
+hipError_t launch_sparse_decode(const DecodeParams &prm, int D, int B, hipStream_t stream);
 hipError_t launch_dequant_pages(const DequantParams &prm, int D, hipStream_t stream);
 
 // number of waves per decode workgroup
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWaves = 8;
 
 }  // namespace qsa

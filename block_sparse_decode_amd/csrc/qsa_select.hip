@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kSelNT) void select_topk_kernel(SelectParams prm)
     if (j >= R) return;
     const int row = r0 + j;
     const int MP = prm.MP, KW = prm.k + prm.W;
-    const RowGeom geo = row_geom(prm.seq_lens[b], r1 - r0, j, prm.P, MP);
+    const RowGeom geo = row_geom(prm.seq_lens[b], r1 - r0, j, prm.log2P, MP);
     const int n = geo.pages;
     const int wlo = n - prm.W > 0 ? n - prm.W : 0;
     const int C = (MP + kSelNT - 1) / kSelNT;          // columns per thread (contiguous)
