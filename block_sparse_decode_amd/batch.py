@@ -99,8 +99,9 @@ class DeviceBatch:
         return torch.empty((self.num_rows, self.q_heads), dtype=torch.float32, device=self.q.device)
 
     def new_workspace(self, num_splits: int = 0) -> Optional[torch.Tensor]:
+        """Zero-filled, as qsa_sparse_decode requires of a workspace on its first use."""
         n = qsa_workspace_bytes(self.shape(), num_splits)
-        return torch.empty(max(n, 16), dtype=torch.uint8, device=self.q.device)
+        return torch.zeros(max(n, 16), dtype=torch.uint8, device=self.q.device)
 
 
 class Step:

@@ -44,11 +44,33 @@ qsa_status check_rows_ptrs(const qsa_paged *pg)
     return QSA_OK;
 }
 
-// 16-column tiles of a request's (rows x q heads per KV head) query columns
+constexpr int kCUs = 256;
+
+// Query columns per tile. A request's columns for one KV head are its R rows x G q heads
+// (row-major); a tile is a run of at most 16 of them (one MFMA N tile), and every page
+// that any of the tile's rows selected is read once for the whole tile. Tiles hold whole
+// rows when G <= 16. Grouping more rows per tile saves reads of pages that several rows
+// selected, but leaves fewer independent tiles; when the batch has fewer tiles than CUs
+// the remaining parallelism must come from splitting a tile's pages across workgroups,
+// which costs a merge of the splits. So rows per tile are halved while that keeps too
+// few tiles, down to one row.
+int tile_cols(const qsa_shape *sh)
+{
+    const int G = sh->num_q_heads / sh->num_kv_heads;
+    if (G >= 16) return 16;
+    int rows = std::max(1, std::min(sh->max_rows_per_request, 16 / G));
+    auto tiles = [&](int r) {
+        return (int64_t)sh->num_requests * sh->num_kv_heads * ((sh->max_rows_per_request + r - 1) / r);
+    };
+    while (rows > 1 && tiles(rows) < kCUs) rows = (rows + 1) / 2;
+    return rows * G;
+}
+
 int col_tiles(const qsa_shape *sh)
 {
     const int cols = sh->max_rows_per_request * (sh->num_q_heads / sh->num_kv_heads);
-    return (cols + 15) / 16;
+    const int tw = tile_cols(sh);
+    return (cols + tw - 1) / tw;
 }
 
 // Splits per (request, KV head, column tile) when the caller leaves the choice to the
@@ -61,9 +83,9 @@ int auto_splits(const qsa_shape *sh)
     const int64_t base = (int64_t)sh->num_requests * sh->num_kv_heads * col_tiles(sh);
     if (base <= 0) return 1;
     const int G = sh->num_q_heads / sh->num_kv_heads;
-    const int64_t rows_per_tile = std::max<int64_t>(1, std::min<int64_t>(sh->max_rows_per_request, (16 + G - 1) / G));
+    const int64_t rows_per_tile = std::max<int64_t>(1, std::min<int64_t>(sh->max_rows_per_request, tile_cols(sh) / G));
     const int64_t union_est = std::min<int64_t>(rows_per_tile * (sh->topk + sh->window), sh->max_pages);
-    int64_t s = (256 + base - 1) / base;
+    int64_t s = (kCUs + base - 1) / base;
     const int64_t cap = std::max<int64_t>(1, union_est / kDecodeWaves);
     s = std::min(s, cap);
     s = std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits));
@@ -76,13 +98,24 @@ int resolve_splits(const qsa_shape *sh, int32_t num_splits)
     return num_splits > kMaxSplits ? kMaxSplits : num_splits;
 }
 
+int64_t decode_tiles(const qsa_shape *sh)
+{
+    return (int64_t)sh->num_requests * sh->num_kv_heads * col_tiles(sh);
+}
+
+// Workspace of a split decode: one counter per tile first (so that their place does not
+// depend on the split count and a workspace can serve calls with different counts), then
+// the partials of every (tile, split).
+size_t decode_counter_bytes(const qsa_shape *sh)
+{
+    return ((size_t)decode_tiles(sh) * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
 size_t decode_ws_bytes(const qsa_shape *sh, int splits)
 {
     if (splits <= 1) return 0;
-    const size_t per = (size_t)sh->num_rows * sh->num_q_heads;
-    const size_t o = (size_t)splits * per * sh->head_dim * sizeof(float);
-    const size_t ml = (size_t)splits * per * 2 * sizeof(float);
-    return ((o + 255) & ~(size_t)255) + ml;
+    return decode_counter_bytes(sh) +
+           (size_t)decode_tiles(sh) * splits * decode_part_floats(sh->head_dim) * sizeof(float);
 }
 
 }  // namespace
@@ -203,13 +236,9 @@ qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uin
     prm.selected = selected;
     prm.out = out;
     prm.lse = lse;
-    prm.part_o = need ? reinterpret_cast<float *>(workspace) : nullptr;
-    prm.part_ml = nullptr;
-    if (need) {
-        const size_t per = (size_t)sh->num_rows * sh->num_q_heads;
-        const size_t o = (size_t)splits * per * sh->head_dim * sizeof(float);
-        prm.part_ml = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + ((o + 255) & ~(size_t)255));
-    }
+    prm.counters = need ? reinterpret_cast<uint32_t *>(workspace) : nullptr;
+    prm.part = need ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + decode_counter_bytes(sh))
+                    : nullptr;
     prm.err = pg->error_word;
     prm.NP = sh->num_phys_pages;
     prm.N = sh->num_rows;
@@ -222,9 +251,12 @@ qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uin
     prm.rmax = sh->max_rows_per_request;
     prm.splits = splits;
     prm.col_tiles = col_tiles(sh);
+    prm.tile_cols = tile_cols(sh);
+    if (decode_tiles(sh) * splits > (int64_t)1 << 30) return QSA_ERR_UNSUPPORTED;
+    prm.tiles = (int)decode_tiles(sh);
     prm.qk_scale_log2 = (float)((double)sh->sm_scale * (double)pg->k_global * 1.4426950408889634);
     prm.v_global = pg->v_global;
-    hipError_t e = launch_sparse_decode(prm, sh->head_dim, sh->num_requests, (hipStream_t)stream);
+    hipError_t e = launch_sparse_decode(prm, sh->head_dim, (hipStream_t)stream);
     return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
 }
 

@@ -5,22 +5,32 @@
 // with a per-row merge. PR #20276, "What runs on the fast paths": K/V tiles are read once
 // per group of rows of one request.
 //
-// Work item: (split s, KV head g, request b), one workgroup of 4 waves.
-//  1. The rows of request b (1..4 causal verify rows) each list their selected pages. The
-//     workgroup builds the union of those pages, each with a row bitmask, in ascending
-//     page order in LDS, and drops entries whose page-table entry is -1. Each page of the
-//     union is read once for all rows.
-//  2. Split s takes a contiguous share of the union. Its waves take the pages round-robin
-//     and run an online softmax over 32-token sub-chunks.
+// Work item: a tile is (request b, KV head g, a run of at most 16 of the request's R x G
+// query columns, whole rows when G <= 16); each tile is split S ways, one 8-wave workgroup
+// per (tile, split). The host picks the rows per tile and S (see tile_cols and auto_splits
+// in qsa_api.hip): rows are grouped only while that still leaves a tile per CU, since
+// splitting a tile's pages instead costs a merge.
+//  1. The tile's rows (up to 4 causal verify rows) each list their selected pages. Wave 0
+//     builds the union of those pages, each with a row bitmask, in LDS, and drops entries
+//     whose page-table entry is -1. Each page of the union is read once for all the
+//     tile's rows.
+//  2. The union's 32-token sub-chunks are numbered page-major. Split s takes a contiguous
+//     range of them and its waves deal that range round-robin, so waves differ by at most
+//     one sub-chunk. Each wave runs an online softmax over its sub-chunks:
 //       S^T = K Q^T   (16x16x32 f16 MFMA; A = K dequantised straight from the global loads,
-//                      B = the request's q rows x G heads, 16 columns per tile)
+//                      B = the tile's q columns, from LDS)
 //       O^T += V^T P^T (A = V^T read from LDS with ds_read_b64_tr_b16, B = P from the
 //                      S^T accumulators, so P never leaves registers)
-//     Each lane's columns mask tokens past its row's length (causal verify rows) and pages
+//     Each lane's column masks tokens past its row's length (causal verify rows) and pages
 //     its row did not select.
 //  3. The waves merge in LDS in a fixed order. With one split the workgroup writes the
-//     final bf16 output and the LSE. Otherwise it writes partials, and the merge kernel
-//     combines the splits in ascending split order.
+//     final bf16 output and the LSE (the lean one-split form). Otherwise it writes its
+//     partial and bumps the tile's counter; the tile's last split to finish merges all S
+//     partials in ascending split order (so the result does not depend on which split is
+//     last), writes the output and puts the counter back to zero for the next call.
+// Workgroups are dispatched round-robin over the 8 XCDs by linear id; the id -> (tile,
+// split) map keeps a tile's splits on one XCD, so the partials the last split reads are
+// in that XCD's L2.
 // NVFP4 -> f16 is exact (see nvfp4_dequant8). The global scales fold into the logit scale
 // and the output.
 #include "qsa_device.hpp"
@@ -29,6 +39,8 @@
 namespace qsa {
 
 constexpr int kMaxUnion = 1024;     // rows (<= 4) x (k + W) (<= 256)
+constexpr int kMaxPages = 4096;     // page-table stride MP
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ void wave_lds_fence()
 {
@@ -106,34 +118,37 @@ __device__ __forceinline__ void load_unit(const DecodeParams &prm, int phys, int
 // different bank groups, and the transposed reads (4 rows x 2 chunks per 16 lanes) do too.
 __device__ __forceinline__ int vswz(int row) { return ((row << 1) + ((row >> 3) & 1)) & 15; }
 
-// Position in a wave's list of 32-token sub-chunks (entry e of the union, sub-chunk c).
+// A wave's position in its split's range of sub-chunks. Sub-chunk u is sub-chunk
+// u mod (P/32) of union entry u / (P/32); sub-chunks that no row of the tile can see (past
+// the longest row's length) are skipped.
 struct UnitCursor {
-    int e, c;
+    int u, c;
     uint32_t pm;
     int phys;
     bool have;
 };
 
-__device__ __forceinline__ UnitCursor first_unit(int e, int e_hi, const uint32_t *u_pm, const int32_t *u_phys)
-{
-    UnitCursor u;
-    u.e = e;
-    u.c = 0;
-    u.have = e < e_hi;
-    u.pm = u.have ? __builtin_amdgcn_readfirstlane(u_pm[e]) : 0u;
-    u.phys = u.have ? __builtin_amdgcn_readfirstlane(u_phys[e]) : 0;
-    return u;
-}
-
-__device__ __forceinline__ UnitCursor next_unit(UnitCursor u, int stride, int e_hi, const uint32_t *u_pm,
+__device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const uint32_t *u_pm,
                                                 const int32_t *u_phys)
 {
-    if (!u.have) return u;
-    if (u.c + 1 < (int)(u.pm >> 24)) {
-        u.c += 1;
-        return u;
+    UnitCursor r;
+    r.have = false;
+    r.c = 0;
+    r.pm = 0u;
+    r.phys = 0;
+    for (; u < u_hi; u += kDecodeWaves) {
+        const uint32_t pm = __builtin_amdgcn_readfirstlane(u_pm[u >> lc]);
+        const int c = u & ((1 << lc) - 1);
+        if (c < (int)(pm >> 24)) {
+            r.have = true;
+            r.c = c;
+            r.pm = pm;
+            r.phys = __builtin_amdgcn_readfirstlane(u_phys[u >> lc]);
+            break;
+        }
     }
-    return first_unit(u.e + stride, e_hi, u_pm, u_phys);
+    r.u = u;
+    return r;
 }
 
 template <int D>
@@ -147,115 +162,145 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     // A column's running max is raised only when a logit exceeds it by more than this
     // (log2 units), so most sub-chunks skip the rescale; P stays <= 2^8 in f16.
     constexpr float kLazy = 8.0f;
-    static_assert((NW / 2) * (NDT + 1) * 64 * 16 <= NW * 32 * D * 2, "merge slots must fit the V staging area");
+    static_assert((NW - 2) * (NDT + 1) * 64 * 16 <= NW * 32 * D * 2, "merge slots must fit the V staging area");
     static_assert(D / 8 <= 16, "one V row holds at most 16 swizzled chunks");
 
-    __shared__ __attribute__((aligned(16))) half_t vsm[NW][32 * D];
+    // One LDS area: the union build's scratch (row-mask bitmap, page-table row, owner of each
+    // page), then the per-wave V staging tiles, then the wave merge slots.
+    constexpr int kStageBytes = NW * 32 * D * 2;
+    constexpr int kScratchBytes = 4 * (kMaxPages / 4 + 2 * kMaxPages);
+    __shared__ __attribute__((aligned(16))) char lds_area[kStageBytes > kScratchBytes ? kStageBytes : kScratchBytes];
+    half_t(*vsm)[32 * D] = reinterpret_cast<half_t(*)[32 * D]>(lds_area);
     __shared__ uint32_t u_pm[kMaxUnion];    // page | row mask << 16 | sub-chunks << 24
     __shared__ int32_t u_phys[kMaxUnion];
     __shared__ float ml_m[NW][16];
     __shared__ uint32_t scan_tmp[NT / 64 + 1];
     __shared__ f16x8 q_lds[KS][64];         // the tile's q operand, in MFMA B-operand lane order
 
-    const int s = blockIdx.x, b = blockIdx.z;
+    const int S = prm.splits;
+    const int wg = blockIdx.x;
+    const int rr = wg / kXcds;
+    const int s = rr % S;
+    const int tile = (rr / S) * kXcds + (wg - rr * kXcds);
+    if (tile >= prm.tiles) return;
     const int T = prm.col_tiles;
-    const int g = blockIdx.y / T, ct = blockIdx.y - g * T;
+    const int HT = prm.Hkv * T;
+    const int b = tile / HT;
+    const int g = (tile - b * HT) / T, ct = tile - b * HT - g * T;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int gq = lane >> 4, li = lane & 15;
     const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
-    const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, tid == 0 && s == 0 && blockIdx.y == 0);
+    const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, tid == 0 && s == 0 && tile == b * HT);
     const int Rb = r1 - r0;         // the request's own row count fixes each row's length
     const int G = prm.Hq / prm.Hkv;
-    const int col0 = ct * 16;       // this tile: columns col0..col0+15 of the request's R x G
+    const int TW = prm.tile_cols;   // this tile: columns col0 .. col0 + TW - 1 of the request's R x G
+    const int col0 = ct * TW;
     if (col0 >= R * G) return;
     const int j_lo = col0 / G;
-    const int j_hi = min(R - 1, (col0 + 15) / G);
+    const int j_hi = min(R - 1, (col0 + TW - 1) / G);
     const int nrow = j_hi - j_lo + 1;                // rows of this tile (<= 4)
     const int MP = prm.MP, P = prm.P, KW = prm.KW;
     const int64_t Lb = prm.seq_lens[b];
 
-    // ---- 1. union of the tile's rows' selected pages --------------------------------
-    // LDS scratch in the V staging area: this request's page-table row and a row-mask
-    // bitmap (one byte per page). Both the page-table row and the selection rows are read
-    // right away, so the union costs one dependent global round trip.
+    // ---- 1. union of the tile's rows' selected pages; the q operand ------------------
+    // All threads stage this request's page-table row in LDS (scratch in the V staging
+    // area, with a row-mask bitmap of one byte per page and an owner word per page) while
+    // wave 0 loads the tile's selection rows and wave 1 loads q, so the union costs one
+    // dependent global round trip. Then wave 0 alone builds the union: each listed page
+    // ORs its row into the bitmap and bids its entry index for the page's owner word (the
+    // smallest bid wins), and each page's owner appends it, with ballot counts for the
+    // positions, so no workgroup barrier is needed. Meanwhile wave 1 converts q into the
+    // MFMA B operand in LDS. Union order: by first listing (rows in order), a function
+    // of the input alone.
     const int nwords = ((MP + 3) / 4 + 3) & ~3;
-    uint32_t *bm = reinterpret_cast<uint32_t *>(&vsm[0][0]);
+    uint32_t *bm = reinterpret_cast<uint32_t *>(lds_area);
     int32_t *pt_row = reinterpret_cast<int32_t *>(bm + nwords);
+    uint32_t *owner = reinterpret_cast<uint32_t *>(pt_row + MP);
     for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
-    for (int p = tid; p < MP; p += NT) pt_row[p] = prm.page_table[(int64_t)b * MP + p];
-    constexpr int kSelPerThread = (kMaxUnion + NT - 1) / NT;
-    int selp[kSelPerThread];
+    for (int p = tid; p < MP; p += NT) {
+        pt_row[p] = prm.page_table[(int64_t)b * MP + p];
+        owner[p] = 0xffffffffu;
+    }
+    const int nent = nrow * KW;                      // <= kMaxUnion
+    constexpr int kSelPerLane = kMaxUnion / 64;
+    int selp[kSelPerLane];
 #pragma unroll
-    for (int i = 0; i < kSelPerThread; ++i) {
-        const int idx = tid + i * NT;
+    for (int i = 0; i < kSelPerLane; ++i) {
+        const int idx = lane + i * 64;
         selp[i] = -1;
-        if (idx < nrow * KW) {
-            const int jr = idx / KW, e = idx - jr * KW;
-            selp[i] = prm.selected[(int64_t)(r0 + j_lo + jr) * KW + e];
+        if (wave == 0 && idx < nent) {
+            const int jr = idx / KW;
+            selp[i] = prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)];
         }
     }
-    __syncthreads();
+    // this lane's query column
+    const int col = col0 + li;
+    const int jc = col / G;                           // row of this lane's column
+    const bool colv = li < TW && jc < R;              // false: padding column
+    uint4 qraw[KS];
 #pragma unroll
-    for (int i = 0; i < kSelPerThread; ++i) {
-        const int idx = tid + i * NT;
-        if (idx >= nrow * KW) break;
-        const int jr = idx / KW;
-        const int p = selp[i];
-        if (p < -1 || p >= MP) {
-            set_error(prm.err, QSA_DEVERR_SELECTED);
-            continue;
-        }
-        if (p < 0 || p >= row_geom(Lb, Rb, j_lo + jr, prm.log2P, MP).pages) continue;   // no visible token
-        const int phys = pt_row[p];
-        if (phys == -1) continue;
-        if (phys < -1 || (int64_t)phys >= prm.NP) {
-            set_error(prm.err, QSA_DEVERR_PAGE_ID);
-            continue;
-        }
-        atomicOr(&bm[p >> 2], 1u << ((p & 3) * 8 + jr));
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = make_uint4(0u, 0u, 0u, 0u);
+    if (wave == 1 && colv) {
+        const int h = g * G + (col - jc * G);
+        const uint4 *qp = reinterpret_cast<const uint4 *>(prm.q + ((int64_t)(r0 + jc) * prm.Hq + h) * D + gq * DQ);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qraw[ks] = qp[ks];
     }
     __syncthreads();
-    uint32_t U;
-    {
-        const int CW = (nwords + NT - 1) / NT;
-        uint32_t cnt = 0;
-        for (int w = tid * CW; w < (tid + 1) * CW && w < nwords; ++w) {
-            const uint32_t x = bm[w];
-            cnt += ((x & 0xffu) != 0) + ((x & 0xff00u) != 0) + ((x & 0xff0000u) != 0) + ((x >> 24) != 0);
+    if (wave == 0) {
+        int phys_e[kSelPerLane];
+#pragma unroll
+        for (int i = 0; i < kSelPerLane; ++i) {
+            phys_e[i] = -1;
+            const int idx = lane + i * 64;
+            if (i * 64 >= nent) break;
+            if (idx >= nent) continue;
+            const int jr = idx / KW;
+            const int p = selp[i];
+            if (p < -1 || p >= MP) {
+                set_error(prm.err, QSA_DEVERR_SELECTED);
+                continue;
+            }
+            if (p < 0 || p >= row_geom(Lb, Rb, j_lo + jr, prm.log2P, MP).pages) continue;   // no visible token
+            const int phys = pt_row[p];
+            if (phys == -1) continue;
+            if (phys < -1 || (int64_t)phys >= prm.NP) {
+                set_error(prm.err, QSA_DEVERR_PAGE_ID);
+                continue;
+            }
+            phys_e[i] = phys;
+            atomicOr(&bm[p >> 2], 1u << ((p & 3) * 8 + jr));
+            atomicMin(&owner[p], (uint32_t)idx);
         }
-        uint32_t pos = block_exclusive_scan<NT>(cnt, scan_tmp, &U);
-        for (int w = tid * CW; w < (tid + 1) * CW && w < nwords; ++w) {
-            const uint32_t x = bm[w];
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const uint32_t m = (x >> (8 * q4)) & 0xffu;
-                if (!m) continue;
-                const int p = 4 * w + q4;
+        wave_lds_fence();
+        uint32_t nu = 0;
+#pragma unroll
+        for (int i = 0; i < kSelPerLane; ++i) {
+            if (i * 64 >= nent) break;
+            const int idx = lane + i * 64;
+            const int p = selp[i];
+            const bool own = phys_e[i] >= 0 && owner[p] == (uint32_t)idx;
+            const uint64_t bal = __ballot(own);
+            if (own) {
+                const uint32_t pos = nu + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+                const uint32_t m = (bm[p >> 2] >> ((p & 3) * 8)) & 0xffu;
                 // sub-chunks of 32 tokens that the longest requesting row can see
                 const int jmax = j_lo + 31 - __builtin_clz(m);     // later rows see more tokens
                 const int64_t vis = row_geom(Lb, Rb, jmax, prm.log2P, MP).len - ((int64_t)p << prm.log2P);
                 const int nc = (int)(vis >= P ? P / 32 : (vis + 31) / 32);
                 u_pm[pos] = (uint32_t)p | (m << 16) | ((uint32_t)nc << 24);
-                u_phys[pos] = pt_row[p];
-                ++pos;
+                u_phys[pos] = phys_e[i];
             }
+            nu += (uint32_t)__builtin_popcountll(bal);
         }
-    }
-
-    // ---- 2. q operand of this lane's column --------------------------------------
-    const int col = col0 + li;
-    const int jc = col / G;                           // row of this lane's column
-    const bool colv = jc < R;                         // false: padding column
-    const int jbit = colv ? jc - j_lo : 31;           // its bit in a page's row mask
-    const int64_t lcol = colv ? row_geom(Lb, Rb, jc, prm.log2P, MP).len : 0;
-    bool qbad = false;
-    if (wave == 0) {
+        if (lane == 0) scan_tmp[0] = nu;
+    } else if (wave == 1) {
+        bool qbad = false;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             f16x8 v = {};
             if (colv) {
-                const int h = g * G + (col - jc * G);
-                const uint4 raw = *reinterpret_cast<const uint4 *>(
-                    prm.q + ((int64_t)(r0 + jc) * prm.Hq + h) * D + gq * DQ + ks * 8);
+                const uint4 raw = qraw[ks];
                 const float f[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
                                     bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
 #pragma unroll
@@ -267,13 +312,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
             }
             q_lds[ks][lane] = v;
         }
+        if (qbad) set_error(prm.err, QSA_DEVERR_Q_RANGE);
     }
-    if (qbad) set_error(prm.err, QSA_DEVERR_Q_RANGE);
-    __syncthreads();                 // union list ready; the scratch area becomes V staging
+    __syncthreads();                 // union list and q ready; the scratch area becomes V staging
+    const uint32_t U = scan_tmp[0];
+    const int jbit = colv ? jc - j_lo : 31;           // the lane's bit in a page's row mask
+    const int64_t lcol = colv ? row_geom(Lb, Rb, jc, prm.log2P, MP).len : 0;
 
     // ---- 3. online softmax over this wave's sub-chunks, the next one in flight -----
-    const int S = prm.splits;
-    const int e_lo = (s * (int)U) / S, e_hi = ((s + 1) * (int)U) / S;
+    const int lc = prm.log2P - 5;                   // log2(sub-chunks per page)
+    const int NU = (int)U << lc;
+    const int u_lo = (int)(((int64_t)s * NU) / S), u_hi = (int)(((int64_t)(s + 1) * NU) / S);
     const float c1 = prm.qk_scale_log2;
     const float NEG_INF = -__builtin_inff();
 
@@ -292,7 +341,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     // LDS) before the next sub-chunk's loads are issued into the same registers; those loads
     // are then in flight during the softmax and the P.V products.
     RawTile<D> kr[2], vr[2];
-    auto process = [&](const UnitCursor &u, const UnitCursor &un) {
+    auto process = [&](const UnitCursor &u, const UnitCursor &un, RawTile<D>(&kr)[2], RawTile<D>(&vr)[2]) {
         const int p = (int)(u.pm & 0xffffu);
         const uint32_t rmask = (u.pm >> 16) & 0xffu;
         const int64_t tok0 = ((int64_t)p << prm.log2P) + u.c * 32;
@@ -376,11 +425,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         oacc[NDT] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop, oacc[NDT], 0, 0, 0);
     };
 
-    UnitCursor u = first_unit(e_lo + wave, e_hi, u_pm, u_phys);
+    UnitCursor u = seek_unit(u_lo + wave, u_hi, lc, u_pm, u_phys);
     if (u.have) load_unit<D>(prm, u.phys, g, u.c, li, gq, kr, vr);
     while (u.have) {
-        const UnitCursor un = next_unit(u, NW, e_hi, u_pm, u_phys);
-        process(u, un);
+        const UnitCursor un = seek_unit(u.u + NW, u_hi, lc, u_pm, u_phys);
+        process(u, un, kr, vr);
         u = un;
     }
 
@@ -396,103 +445,118 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         for (int dt = 0; dt <= NDT; ++dt) oacc[dt] *= wgt;
         m_col = M;                   // common reference max of the column
     }
-    // slot layout [slot][dt][lane] f32x4: every lane moves 16 contiguous bytes
+    // Two levels in a fixed order: waves 2 .. NW-1 publish, waves 0 and 1 add the even and
+    // the odd ones in ascending order; then wave 1 publishes and wave 0 adds.
+    // Slot layout [slot][dt][lane] f32x4: every lane moves 16 contiguous bytes.
     f32x4 *slots = reinterpret_cast<f32x4 *>(&vsm[0][0]);
     constexpr int kSlot = (NDT + 1) * 64;
+    if (wave >= 2) {
 #pragma unroll
-    for (int half = NW / 2; half >= 1; half /= 2) {
-        if (wave >= half && wave < 2 * half) {
-#pragma unroll
-            for (int dt = 0; dt <= NDT; ++dt) slots[(wave - half) * kSlot + dt * 64 + lane] = oacc[dt];
-        }
-        __syncthreads();
-        if (wave < half) {
-#pragma unroll
-            for (int dt = 0; dt <= NDT; ++dt) oacc[dt] += slots[wave * kSlot + dt * 64 + lane];
-        }
-        __syncthreads();
+        for (int dt = 0; dt <= NDT; ++dt) slots[(wave - 2) * kSlot + dt * 64 + lane] = oacc[dt];
     }
-    if (wave != 0 || !colv) return;
+    __syncthreads();
+    if (wave < 2) {
+        for (int w = wave + 2; w < NW; w += 2) {
+#pragma unroll
+            for (int dt = 0; dt <= NDT; ++dt) oacc[dt] += slots[(w - 2) * kSlot + dt * 64 + lane];
+        }
+    }
+    __syncthreads();
+    if (wave == 1) {
+#pragma unroll
+        for (int dt = 0; dt <= NDT; ++dt) slots[dt * 64 + lane] = oacc[dt];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int dt = 0; dt <= NDT; ++dt) oacc[dt] += slots[dt * 64 + lane];
+    }
+    if (wave != 0) return;
+    if (S > 1) {
+        // Publish this split's partial, count it, and let the tile's last split merge.
+        // The partial moves through agent-scope (coherent) stores and loads: each such access
+        // is coherent across the XCDs' L2s on its own, so the handoff needs only the stores'
+        // completion (vmcnt 0) before the count -- not an agent-scope fence, whose L2
+        // writeback and invalidate cost several microseconds per workgroup here.
+        constexpr int PF = decode_part_floats(D);
+        constexpr int kOff = (NDT + 1) * 64 * 4;
+        float *tile_part = prm.part + (int64_t)tile * S * PF;
+        float *mine = tile_part + (int64_t)s * PF;
+#pragma unroll
+        for (int dt = 0; dt <= NDT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __hip_atomic_store(mine + (dt * 4 + i) * 64 + lane, oacc[dt][i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + kOff + lane, m_col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): the partial's stores are complete
+        uint32_t done = 0u;
+        if (lane == 0) done = __hip_atomic_fetch_add(prm.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        done = __builtin_amdgcn_readfirstlane(done);
+        if (done != (uint32_t)(S - 1)) return;
+        // the last split: every other partial's stores completed before its count
+        float M = NEG_INF;
+        for (int sp = 0; sp < S; ++sp)
+            M = fmaxf(M, sp == s ? m_col
+                                 : __hip_atomic_load(tile_part + (int64_t)sp * PF + kOff + lane, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+        f32x4 acc[NDT + 1];
+#pragma unroll
+        for (int dt = 0; dt <= NDT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < S; ++sp) {         // ascending split order
+            const float *part = tile_part + (int64_t)sp * PF;
+            f32x4 o[NDT + 1];
+            float m;
+            if (sp == s) {
+#pragma unroll
+                for (int dt = 0; dt <= NDT; ++dt) o[dt] = oacc[dt];
+                m = m_col;
+            } else {
+#pragma unroll
+                for (int dt = 0; dt <= NDT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[dt][i] = __hip_atomic_load(part + (dt * 4 + i) * 64 + lane, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                m = __hip_atomic_load(part + kOff + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            const float wgt = (m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+#pragma unroll
+            for (int dt = 0; dt <= NDT; ++dt) acc[dt] += wgt * o[dt];
+        }
+#pragma unroll
+        for (int dt = 0; dt <= NDT; ++dt) oacc[dt] = acc[dt];
+        m_col = M;
+        if (lane == 0) __hip_atomic_store(prm.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!colv) return;
     const int row = r0 + jc, head = g * G + (col - jc * G);
     const float L = oacc[NDT][0];
-    if (S == 1) {
-        const float sc = (L > 0.0f) ? prm.v_global / L : 0.0f;
+    const float sc = (L > 0.0f) ? prm.v_global / L : 0.0f;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const f32x4 o = oacc[dt] * sc;
-            uint2 packed;
-            packed.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-            packed.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-            *reinterpret_cast<uint2 *>(prm.out + ((int64_t)row * prm.Hq + head) * D + dt * 16 + gq * 4) = packed;
-        }
-        if (gq == 0 && prm.lse)
-            prm.lse[(int64_t)row * prm.Hq + head] = (L > 0.0f) ? (m_col + __log2f(L)) * 0.69314718055994531f : NEG_INF;
-    } else {
-        const int64_t slot = ((int64_t)s * prm.N + row) * prm.Hq + head;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            *reinterpret_cast<f32x4 *>(prm.part_o + slot * D + dt * 16 + gq * 4) = oacc[dt];
-        if (gq == 0) {
-            prm.part_ml[slot * 2] = m_col;
-            prm.part_ml[slot * 2 + 1] = L;
-        }
+    for (int dt = 0; dt < NDT; ++dt) {
+        const f32x4 o = oacc[dt] * sc;
+        uint2 packed;
+        packed.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+        packed.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+        *reinterpret_cast<uint2 *>(prm.out + ((int64_t)row * prm.Hq + head) * D + dt * 16 + gq * 4) = packed;
     }
-}
-
-// Combine the splits of every (row, q head): ascending split order, one thread per 4 outputs.
-template <int D>
-__global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams prm)
-{
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)prm.N * prm.Hq * (D / 4);
-    if (idx >= total) return;
-    const int64_t rh = idx / (D / 4);
-    const int d4 = (int)(idx - rh * (D / 4));
-    const int S = prm.splits;
-    const int64_t stride = (int64_t)prm.N * prm.Hq;
-    const float NEG_INF = -__builtin_inff();
-    float M = NEG_INF;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, prm.part_ml[(s * stride + rh) * 2]);
-    float L = 0.0f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (M != NEG_INF) {
-        for (int s = 0; s < S; ++s) {
-            const float m = prm.part_ml[(s * stride + rh) * 2];
-            const float w = __builtin_amdgcn_exp2f(m - M);
-            L += prm.part_ml[(s * stride + rh) * 2 + 1] * w;
-            o += *reinterpret_cast<const f32x4 *>(prm.part_o + (s * stride + rh) * D + 4 * d4) * w;
-        }
-    }
-    uint2 packed;
-    float lse_v;
-    if (L > 0.0f) {
-        const float sc = prm.v_global / L;
-        packed.x = (uint32_t)f32_to_bf16_rne(o[0] * sc) | ((uint32_t)f32_to_bf16_rne(o[1] * sc) << 16);
-        packed.y = (uint32_t)f32_to_bf16_rne(o[2] * sc) | ((uint32_t)f32_to_bf16_rne(o[3] * sc) << 16);
-        lse_v = (M + __log2f(L)) * 0.69314718055994531f;
-    } else {
-        packed.x = packed.y = 0u;
-        lse_v = NEG_INF;
-    }
-    *reinterpret_cast<uint2 *>(prm.out + rh * D + 4 * d4) = packed;
-    if (d4 == 0 && prm.lse) prm.lse[rh] = lse_v;
+    if (gq == 0 && prm.lse)
+        prm.lse[(int64_t)row * prm.Hq + head] = (L > 0.0f) ? (m_col + __log2f(L)) * 0.69314718055994531f : NEG_INF;
 }
 
 template <int D>
-static hipError_t launch_decode_d(const DecodeParams &prm, int B, hipStream_t stream)
+static hipError_t launch_decode_d(const DecodeParams &prm, hipStream_t stream)
 {
-    dim3 grid(prm.splits, prm.Hkv * prm.col_tiles, B);
+    const int64_t groups = (prm.tiles + kXcds - 1) / kXcds;
+    const unsigned grid = (unsigned)(groups * kXcds * prm.splits);
     sparse_decode_kernel<D><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || prm.splits == 1) return e;
-    const int64_t total = (int64_t)prm.N * prm.Hq * (D / 4);
-    if (total > 0) merge_splits_kernel<D><<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(prm);
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_decode(const DecodeParams &prm, int D, int B, hipStream_t stream)
+hipError_t launch_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream)
 {
-    return D == 64 ? launch_decode_d<64>(prm, B, stream) : launch_decode_d<128>(prm, B, stream);
+    return D == 64 ? launch_decode_d<64>(prm, stream) : launch_decode_d<128>(prm, stream);
 }
 
 // ---- parity hook: whole pages through the same decode as the attention kernel ----------

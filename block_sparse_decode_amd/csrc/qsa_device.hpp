@@ -127,16 +127,23 @@ __device__ __forceinline__ float sum_across_groups(float v)
 // Block-wide exclusive prefix sum of one uint32 per thread (blockDim.x = NT, a multiple
 // of 64). `tmp` holds NT / 64 + 1 words of LDS. Returns the exclusive prefix; *total gets
 // the block sum. Contains __syncthreads().
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t *total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) tmp[wave] = x;
     __syncthreads();
     if (threadIdx.x == 0) {

@@ -42,11 +42,12 @@ struct DecodeParams {
     const int32_t *selected;
     uint16_t *out;
     float *lse;
-    float *part_o;            // [S][N][Hq][D] unnormalised partial outputs (S > 1)
-    float *part_ml;           // [S][N][Hq][2] (max in log2 units, sum)
+    float *part;              // [tiles][S][decode_part_floats(D)] partials of split tiles (S > 1)
+    uint32_t *counters;       // [tiles] splits finished per tile; zero between calls (S > 1)
     uint32_t *err;
     int64_t NP;
-    int N, MP, P, log2P, KW, Hq, Hkv, rmax, splits, col_tiles;
+    int N, MP, P, log2P, KW, Hq, Hkv, rmax, splits, col_tiles, tiles;
+    int tile_cols;            // query columns (rows x q heads of one KV head) per tile, <= 16
     float qk_scale_log2;      // sm_scale * k_global * log2(e)
     float v_global;
 };
@@ -63,10 +64,15 @@ struct DequantParams {
 
 hipError_t launch_index_scores(const IndexParams &prm, int D, int B, hipStream_t stream);
 hipError_t launch_select_topk(const SelectParams &prm, int B, hipStream_t stream);
-hipError_t launch_sparse_decode(const DecodeParams &prm, int D, int B, hipStream_t stream);
+hipError_t launch_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream);
 hipError_t launch_dequant_pages(const DequantParams &prm, int D, hipStream_t stream);
 
 // number of waves per decode workgroup
 constexpr int kDecodeWaves = 8;
+
+// A split's partial result for one tile (16 query columns): the unnormalised O^T
+// accumulators of the d/16 output tiles and the ones tile (the softmax denominator), laid
+// out [tile][element 0..3][lane], then the column max (log2 units) per lane.
+constexpr int decode_part_floats(int D) { return (D / 16 + 1) * 64 * 4 + 64; }
 
 }  // namespace qsa

@@ -132,7 +132,13 @@ qsa_status qsa_select_topk(const qsa_shape *shape, const qsa_paged *paged,
 
 /*
  * Workspace needed by qsa_sparse_decode for `num_splits` (0 = the library's choice for
- * this shape). Returns 0 when the call needs none. Also 0 for an invalid shape.
+ * this shape). Returns 0 when the call needs none (one split). Also 0 for an invalid shape.
+ * The workspace holds each split's partial result and one completion counter per
+ * (request, KV head, 16-column tile). The counters must be zero when a call starts: fill
+ * a new workspace with zeros once (e.g. hipMemsetAsync) before its first use. Every call
+ * leaves them zero again, so a workspace can be reused by later calls, with any split
+ * count, with no further clearing (also inside captured graphs). Two calls that may
+ * overlap in time must not share a workspace.
  */
 size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
 
@@ -147,8 +153,8 @@ size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
  *   lse        fp32  [N][Hq]        (device, optional: natural-log sum of exp of the logits)
  *   num_splits 0 = the library's choice; > 0 forces that many KV splits per
  *              (request, KV head), clamped to 64
- *   workspace  device scratch of at least qsa_workspace_bytes(shape, num_splits) bytes;
- *              its contents on entry do not matter
+ *   workspace  device scratch of at least qsa_workspace_bytes(shape, num_splits) bytes,
+ *              zero-filled before its first use (see qsa_workspace_bytes)
  * For row j of request b and q head h, the tokens attended are
  *   T = {(p, t): p listed in the row, page_table[b][p] valid, t < P, p * P + t < L}.
  * The output is softmax(sm_scale * k_global * q . K_raw) @ (v_global * V_raw) over T, where

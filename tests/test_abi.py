@@ -129,9 +129,13 @@ def test_pointer_validation():
 def test_workspace_sizing():
     sh = _shape()
     assert q.qsa_workspace_bytes(sh, 1) == 0
-    per = 8 * 32
-    o = 4 * per * 128 * 4
-    assert q.qsa_workspace_bytes(sh, 4) == ((o + 255) // 256) * 256 + 4 * per * 2 * 4
+    # 2 requests x 4 KV heads x 4 tiles: 4 rows x 8 q heads per KV head, one row per tile
+    # (grouping rows would leave fewer tiles than CUs); one uint32 counter per tile (padded
+    # to 256 bytes), then per (tile, split) 9 accumulator tiles (8 of d 128 + the
+    # denominator) of 64 lanes x 4 floats, plus 64 column maxima
+    tiles = 2 * 4 * 4
+    part = tiles * 4 * (9 * 64 * 4 + 64) * 4
+    assert q.qsa_workspace_bytes(sh, 4) == 256 + part
     assert q.qsa_workspace_bytes(sh, 1000) == q.qsa_workspace_bytes(sh, 64)
     # a too-small workspace is refused before any launch
     pg = _paged()

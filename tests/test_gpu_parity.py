@@ -201,6 +201,31 @@ def test_attention_split_invariance_bitwise_per_split_count():
         assert np.all(np.abs(o - outs[0]) <= ATOL + RTOL * np.abs(outs[0]))
 
 
+def test_workspace_reused_across_split_counts():
+    """One zero-filled workspace serves calls with different split counts: every call
+    leaves the per-tile completion counters (the first bytes) zero and matches the oracle."""
+    w = workload(ATT_SMALL[3])
+    b = DeviceBatch.upload(w)
+    st = Step(b, num_splits=7)
+    st.scores_call()
+    st.select_call()
+    torch.cuda.synchronize()
+    sel = st.selected.cpu().numpy()
+    ref_out, ref_lse = oracle.attention(w, sel)
+    sh = b.shape()
+    # the counters come first: workspace(S) = counter bytes + tiles * S * per-split partial
+    part = ((w.cfg.head_dim // 16 + 1) * 64 * 4 + 64) * 4
+    tiles = (q.qsa_workspace_bytes(sh, 3) - q.qsa_workspace_bytes(sh, 2)) // part
+    assert tiles > 0
+    ws = torch.zeros(max(q.qsa_workspace_bytes(sh, sp) for sp in (7, 2, 5, 3)), dtype=torch.uint8, device="cuda")
+    for sp in (7, 2, 5, 3, 7):
+        st.out.fill_(0x1234)
+        q.qsa_sparse_decode(sh, st.paged_, b.q, st.selected, st.out, st.lse, sp, ws, None, None)
+        torch.cuda.synchronize()
+        _check_attention(_u16(st.out), st.lse.cpu().numpy(), ref_out, ref_lse, f"ws reuse splits={sp}")
+        assert int(ws[:tiles * 4].count_nonzero().item()) == 0, f"counters left non-zero after splits={sp}"
+
+
 SAMPLES = 24
 
 
