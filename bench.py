@@ -29,6 +29,71 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse NVFP4 decode attention: µs/step + achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+COPY_BYTES = 1 << 30           # the calibration copy (--copy-calibration)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_decode_{workload}.json")
+
+
+def kernel_source_hash():
+    """SHA-256 over the HIP sources and the header; traffic counters are valid for this hash only."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "block_sparse_decode_amd", "csrc", "*"))) + \
+        [os.path.join(ROOT, "include", "qsa.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_counters(fetch_csv, write_csv, workload):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of this
+    script with --copy-calibration into HBM bytes per sparse_decode_kernel launch.
+
+    Each counter is scaled by what it reads for the calibration copy, a plain device copy of
+    COPY_BYTES read and COPY_BYTES written (the copy dispatch is the one with the largest
+    reading). Writes the result next to the kernel-time summaries, tagged with the source hash.
+    """
+    import csv
+    import statistics
+
+    def load(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        dec = [float(r["Counter_Value"]) for r in rows if "sparse_decode_kernel" in r["Kernel_Name"]]
+        cpy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        assert dec, f"no sparse_decode_kernel dispatch in {path}"
+        return statistics.median(dec), cpy, len(dec)
+
+    f_dec, f_cpy, n_f = load(fetch_csv, "FETCH_SIZE")
+    w_dec, w_cpy, n_w = load(write_csv, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (f_cpy * 1024.0)
+    w_scale = COPY_BYTES / (w_cpy * 1024.0)
+    out = {
+        "kernel": "sparse_decode_kernel", "workload": workload, "source_sha256": kernel_source_hash(),
+        "fetch_kib_per_dispatch_median": f_dec, "write_kib_per_dispatch_median": w_dec,
+        "dispatches": [n_f, n_w],
+        "copy_fetch_kib": f_cpy, "copy_write_kib": w_cpy, "fetch_scale": f_scale, "write_scale": w_scale,
+        "fetch_bytes": f_dec * 1024.0 * f_scale, "write_bytes": w_dec * 1024.0 * w_scale,
+    }
+    out["traffic_bytes"] = out["fetch_bytes"] + out["write_bytes"]
+    path = TRAFFIC_FILE.format(workload=workload)
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed counter runs, if they match this source."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha256") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t["traffic_bytes"]
 
 
 def algorithmic_bytes(w, selected):
@@ -104,10 +169,15 @@ def main():
     ap.add_argument("--workload", default="mtp_verify_32k")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=32, help="rows of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="rows of the CPU-oracle sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for PMC byte-counter scaling)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 counter runs into the traffic file and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -136,7 +206,7 @@ def main():
     steps = [Step(b, num_splits=args.splits) for b in layers]
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
@@ -204,7 +274,7 @@ def main():
                    "timing": "mean of back-to-back launches between one HIP event pair on the launch stream"},
         "bytes": ab,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
                      "kernel": "qsa_sparse_decode (sparse_decode_kernel, plus merge_splits_kernel when split)"},
         "error_word": err,
     }
