@@ -13,7 +13,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (Paged, Shape, qsa_index_scores, qsa_select_topk, qsa_sparse_decode, qsa_workspace_bytes)
+from . import (Paged, Shape, qsa_index_scores, qsa_select_sparse_decode, qsa_select_topk, qsa_sparse_decode,
+               qsa_workspace_bytes)
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:
@@ -107,11 +108,16 @@ class DeviceBatch:
 class Step:
     """One decode / verify step of one attention layer: scores -> selection -> attention.
 
+    fused=True (the default) runs the selection inside the attention launch
+    (qsa_select_sparse_decode); fused=False runs qsa_select_topk, then qsa_sparse_decode.
+    Both give the same selection rows and outputs.
+
     The argument blocks and outputs are built once, so a call only launches kernels.
     """
 
-    def __init__(self, batch: DeviceBatch, num_splits: int = 0, with_lse: bool = True):
+    def __init__(self, batch: DeviceBatch, num_splits: int = 0, with_lse: bool = True, fused: bool = True):
         self.b = batch
+        self.fused = fused
         self.num_splits = num_splits
         self.shape_ = batch.shape()
         self.paged_ = batch.paged()
@@ -131,8 +137,15 @@ class Step:
         qsa_sparse_decode(self.shape_, self.paged_, self.b.q, self.selected if selected is None else selected,
                           self.out, self.lse, self.num_splits, self.ws, None, stream)
 
+    def select_decode_call(self, stream=None):
+        qsa_select_sparse_decode(self.shape_, self.paged_, self.b.q, self.scores, self.selected, self.out, self.lse,
+                                 self.num_splits, self.ws, None, stream)
+
     def __call__(self, stream=None):
         self.scores_call(stream)
-        self.select_call(stream)
-        self.decode_call(stream)
+        if self.fused:
+            self.select_decode_call(stream)
+        else:
+            self.select_call(stream)
+            self.decode_call(stream)
         return self.out

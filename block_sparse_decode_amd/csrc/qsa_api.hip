@@ -200,9 +200,15 @@ size_t qsa_workspace_bytes(const qsa_shape *sh, int32_t num_splits)
     return decode_ws_bytes(sh, resolve_splits(sh, num_splits));
 }
 
-qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const int32_t *selected,
-                             uint16_t *out, float *lse, int32_t num_splits, void *workspace, size_t workspace_bytes,
-                             void *stream)
+}  // extern "C"
+
+namespace {
+
+// Shared by qsa_sparse_decode (scores == NULL: `selected` is an input) and
+// qsa_select_sparse_decode (the selection is computed from `scores` and written to `selected`).
+qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const float *scores,
+                       int32_t *selected, uint16_t *out, float *lse, int32_t num_splits, void *workspace,
+                       size_t workspace_bytes, void *stream)
 {
     qsa_status st = check_shape(sh);
     if (st != QSA_OK) return st;
@@ -212,10 +218,12 @@ qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uin
     if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
     if (!q || !out || !pg->page_table || !pg->k_codes || !pg->k_scales || !pg->v_codes || !pg->v_scales)
         return QSA_ERR_INVALID_ARG;
-    if (sh->topk + sh->window > 0 && !selected) return QSA_ERR_INVALID_ARG;
+    const bool fused = scores != nullptr;
+    const int KW = sh->topk + sh->window;
+    if (KW > 0 && !selected) return QSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out) || !aligned16(pg->page_table) || !aligned16(pg->k_codes) ||
         !aligned16(pg->k_scales) || !aligned16(pg->v_codes) || !aligned16(pg->v_scales) ||
-        (selected && !aligned16(selected)) || (lse && !aligned16(lse)))
+        (selected && !aligned16(selected)) || (lse && !aligned16(lse)) || (fused && !aligned16(scores)))
         return QSA_ERR_INVALID_ARG;
     if (!isfinite(pg->k_global) || !isfinite(pg->v_global)) return QSA_ERR_INVALID_ARG;
     const int splits = resolve_splits(sh, num_splits);
@@ -234,6 +242,7 @@ qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uin
     prm.v_scales = pg->v_scales;
     prm.q = q;
     prm.selected = selected;
+    prm.scores = scores;
     prm.out = out;
     prm.lse = lse;
     prm.counters = need ? reinterpret_cast<uint32_t *>(workspace) : nullptr;
@@ -245,7 +254,9 @@ qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uin
     prm.MP = sh->max_pages;
     prm.P = sh->page_size;
     prm.log2P = sh->page_size == 64 ? 6 : 7;
-    prm.KW = sh->topk + sh->window;
+    prm.KW = KW;
+    prm.k = sh->topk;
+    prm.W = sh->window;
     prm.Hq = sh->num_q_heads;
     prm.Hkv = sh->num_kv_heads;
     prm.rmax = sh->max_rows_per_request;
@@ -256,8 +267,51 @@ qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uin
     prm.tiles = (int)decode_tiles(sh);
     prm.qk_scale_log2 = (float)((double)sh->sm_scale * (double)pg->k_global * 1.4426950408889634);
     prm.v_global = pg->v_global;
-    hipError_t e = launch_sparse_decode(prm, sh->head_dim, (hipStream_t)stream);
+    hipError_t e;
+    if (!fused || KW == 0) {
+        e = launch_sparse_decode(prm, sh->head_dim, (hipStream_t)stream);
+    } else if (sh->max_pages <= 1024) {
+        e = launch_select_sparse_decode(prm, sh->head_dim, (hipStream_t)stream);
+    } else {
+        // wide score tables: the separate selection kernel, then the attention
+        SelectParams sp;
+        sp.seq_lens = pg->seq_lens;
+        sp.row_offsets = pg->row_offsets;
+        sp.scores = scores;
+        sp.selected = selected;
+        sp.err = pg->error_word;
+        sp.N = sh->num_rows;
+        sp.MP = sh->max_pages;
+        sp.P = sh->page_size;
+        sp.log2P = prm.log2P;
+        sp.k = sh->topk;
+        sp.W = sh->window;
+        sp.rmax = sh->max_rows_per_request;
+        e = launch_select_topk(sp, sh->num_requests, (hipStream_t)stream);
+        if (e == hipSuccess) e = launch_sparse_decode(prm, sh->head_dim, (hipStream_t)stream);
+    }
     return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const int32_t *selected,
+                             uint16_t *out, float *lse, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    return decode_call(sh, pg, q, nullptr, const_cast<int32_t *>(selected), out, lse, num_splits, workspace,
+                       workspace_bytes, stream);
+}
+
+qsa_status qsa_select_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const float *scores,
+                                    int32_t *selected, uint16_t *out, float *lse, int32_t num_splits,
+                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (sh && pg && sh->topk + sh->window > 0 && !scores && sh->num_rows > 0 && sh->num_requests > 0)
+        return QSA_ERR_INVALID_ARG;
+    return decode_call(sh, pg, q, scores, selected, out, lse, num_splits, workspace, workspace_bytes, stream);
 }
 
 qsa_status qsa_nvfp4_dequant_pages(const qsa_shape *sh, const uint8_t *codes, const uint8_t *scales,

@@ -35,6 +35,7 @@
 // and the output.
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
+#include "qsa_select_row.hpp"
 
 namespace qsa {
 
@@ -151,7 +152,9 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
     return r;
 }
 
-template <int D>
+// SELC = 0: the rows' selections are an input. SELC = 8 or 16: they are computed here from
+// the scores (select_row with that many columns per lane) and also written out.
+template <int D, int SELC>
 __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(DecodeParams prm)
 {
     constexpr int NW = kDecodeWaves;
@@ -224,13 +227,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     const int nent = nrow * KW;                      // <= kMaxUnion
     constexpr int kSelPerLane = kMaxUnion / 64;
     int selp[kSelPerLane];
+    int32_t *sel_lds = reinterpret_cast<int32_t *>(u_pm);   // the selections, before the union
+    if constexpr (SELC == 0) {
 #pragma unroll
-    for (int i = 0; i < kSelPerLane; ++i) {
-        const int idx = lane + i * 64;
-        selp[i] = -1;
-        if (wave == 0 && idx < nent) {
-            const int jr = idx / KW;
-            selp[i] = prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)];
+        for (int i = 0; i < kSelPerLane; ++i) {
+            const int idx = lane + i * 64;
+            selp[i] = -1;
+            if (wave == 0 && idx < nent) {
+                const int jr = idx / KW;
+                selp[i] = prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)];
+            }
+        }
+    } else {
+        // wave w selects the tile's row j_lo + w, into LDS
+        if (wave < nrow) {
+            const int jw = j_lo + wave;
+            select_row<SELC, false>(prm.scores + (int64_t)(r0 + jw) * MP, MP, row_geom(Lb, Rb, jw, prm.log2P, MP).pages,
+                                    prm.k, prm.W, sel_lds + wave * KW);
         }
     }
     // this lane's query column
@@ -240,7 +253,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     uint4 qraw[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qraw[ks] = make_uint4(0u, 0u, 0u, 0u);
-    if (wave == 1 && colv) {
+    if (wave == NW - 1 && colv) {
         const int h = g * G + (col - jc * G);
         const uint4 *qp = reinterpret_cast<const uint4 *>(prm.q + ((int64_t)(r0 + jc) * prm.Hq + h) * D + gq * DQ);
 #pragma unroll
@@ -248,6 +261,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     }
     __syncthreads();
     if (wave == 0) {
+        if constexpr (SELC > 0) {
+            // this workgroup publishes the rows that start in its tile (KV head 0, split 0)
+#pragma unroll
+            for (int i = 0; i < kSelPerLane; ++i) {
+                const int idx = lane + i * 64;
+                selp[i] = -1;
+                if (i * 64 >= nent) break;
+                if (idx < nent) {
+                    selp[i] = sel_lds[idx];
+                    const int jr = idx / KW;
+                    if (g == 0 && s == 0 && col0 <= (j_lo + jr) * G)
+                        prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)] = selp[i];
+                }
+            }
+            wave_lds_fence();        // the reads of sel_lds are done before u_pm is written
+        }
         int phys_e[kSelPerLane];
 #pragma unroll
         for (int i = 0; i < kSelPerLane; ++i) {
@@ -294,7 +323,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
             nu += (uint32_t)__builtin_popcountll(bal);
         }
         if (lane == 0) scan_tmp[0] = nu;
-    } else if (wave == 1) {
+    } else if (wave == NW - 1) {
         bool qbad = false;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -545,18 +574,25 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         prm.lse[(int64_t)row * prm.Hq + head] = (L > 0.0f) ? (m_col + __log2f(L)) * 0.69314718055994531f : NEG_INF;
 }
 
-template <int D>
+template <int D, int SELC>
 static hipError_t launch_decode_d(const DecodeParams &prm, hipStream_t stream)
 {
     const int64_t groups = (prm.tiles + kXcds - 1) / kXcds;
     const unsigned grid = (unsigned)(groups * kXcds * prm.splits);
-    sparse_decode_kernel<D><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+    sparse_decode_kernel<D, SELC><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream)
 {
-    return D == 64 ? launch_decode_d<64>(prm, stream) : launch_decode_d<128>(prm, stream);
+    return D == 64 ? launch_decode_d<64, 0>(prm, stream) : launch_decode_d<128, 0>(prm, stream);
+}
+
+hipError_t launch_select_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream)
+{
+    if (prm.MP > 1024) return hipErrorInvalidValue;
+    if (prm.MP <= 512) return D == 64 ? launch_decode_d<64, 8>(prm, stream) : launch_decode_d<128, 8>(prm, stream);
+    return D == 64 ? launch_decode_d<64, 16>(prm, stream) : launch_decode_d<128, 16>(prm, stream);
 }
 
 // ---- parity hook: whole pages through the same decode as the attention kernel ----------

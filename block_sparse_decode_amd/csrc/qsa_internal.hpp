@@ -39,7 +39,8 @@ struct DecodeParams {
     const uint8_t *v_codes;
     const uint8_t *v_scales;
     const uint16_t *q;
-    const int32_t *selected;
+    int32_t *selected;        // input, or with the selection fused in: output [N][k + W]
+    const float *scores;      // selection fused in only: [N][MP]
     uint16_t *out;
     float *lse;
     float *part;              // [tiles][S][decode_part_floats(D)] partials of split tiles (S > 1)
@@ -48,6 +49,7 @@ struct DecodeParams {
     int64_t NP;
     int N, MP, P, log2P, KW, Hq, Hkv, rmax, splits, col_tiles, tiles;
     int tile_cols;            // query columns (rows x q heads of one KV head) per tile, <= 16
+    int k, W;                 // selection fused in only
     float qk_scale_log2;      // sm_scale * k_global * log2(e)
     float v_global;
 };
@@ -65,6 +67,9 @@ struct DequantParams {
 hipError_t launch_index_scores(const IndexParams &prm, int D, int B, hipStream_t stream);
 hipError_t launch_select_topk(const SelectParams &prm, int B, hipStream_t stream);
 hipError_t launch_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream);
+// the selection of each tile's rows computed from `scores` inside the attention kernel's
+// prologue (MP <= 1024); `selected` is written as qsa_select_topk writes it
+hipError_t launch_select_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream);
 hipError_t launch_dequant_pages(const DequantParams &prm, int D, hipStream_t stream);
 
 // number of waves per decode workgroup

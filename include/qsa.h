@@ -169,6 +169,21 @@ qsa_status qsa_sparse_decode(const qsa_shape *shape, const qsa_paged *paged,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The selection fused into the attention (PR #20276, Performance > What runs on the fast
+ * paths: the block top-k fused with its expansion to tokens; Decisions worth knowing: the
+ * fast path produces the canonical rows from one launch). Takes the index scores instead
+ * of the selection rows and writes both results: `selected` exactly as qsa_select_topk
+ * writes it and `out` / `lse` exactly as qsa_sparse_decode computes them from it, in one
+ * launch (two when max_pages > 1024). Arguments as for those calls; `scores` fp32 [N][MP]
+ * (device, read only), `selected` int32 [N][k + W] (device, written in full), workspace
+ * as for qsa_sparse_decode.
+ */
+qsa_status qsa_select_sparse_decode(const qsa_shape *shape, const qsa_paged *paged,
+                                    const uint16_t *q, const float *scores, int32_t *selected,
+                                    uint16_t *out, float *lse, int32_t num_splits,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Parity hook: NVFP4 dequantisation of whole pages through the same device decode that
  * qsa_sparse_decode uses (the counterpart of the pages' NVFP4 page -> bf16 conversion,
  * PR #20937, qsa_nvfp4_pages_to_bf16).

@@ -126,6 +126,22 @@ def test_pointer_validation():
                 1 << 30, None) == 2
 
 
+def test_fused_select_decode_validation():
+    sh, pg = _shape(), _paged()
+    # the selection needs the scores and somewhere to write the rows
+    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, None, FAKE, FAKE, None, 0,
+                FAKE, 1 << 30, None) == 1
+    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, None, FAKE, None, 0,
+                FAKE, 1 << 30, None) == 1
+    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE + 4, FAKE, FAKE, None,
+                0, FAKE, 1 << 30, None) == 1
+    # the checks of qsa_sparse_decode apply
+    assert _raw("qsa_select_sparse_decode", ctypes.byref(_shape(head_dim=96)), ctypes.byref(pg), FAKE, FAKE, FAKE,
+                FAKE, None, 0, FAKE, 1 << 30, None) == 2
+    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, None, 4,
+                FAKE, q.qsa_workspace_bytes(sh, 4) - 1, None) == 3
+
+
 def test_workspace_sizing():
     sh = _shape()
     assert q.qsa_workspace_bytes(sh, 1) == 0
@@ -152,6 +168,8 @@ def test_empty_batches_are_no_ops():
     assert _raw("qsa_select_topk", ctypes.byref(sh), ctypes.byref(pg), None, None, None) == 0
     assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), None, None, None, None, 0, None, 0,
                 None) == 0
+    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), None, None, None, None, None, 0,
+                None, 0, None) == 0
     dq = _shape()
     assert _raw("qsa_nvfp4_dequant_pages", ctypes.byref(dq), None, None, ctypes.c_float(1.0), None, 0, None,
                 None) == 0

@@ -226,6 +226,35 @@ def test_workspace_reused_across_split_counts():
         assert int(ws[:tiles * 4].count_nonzero().item()) == 0, f"counters left non-zero after splits={sp}"
 
 
+FUSED_CASES = [(c, sp) for c in ATT_SMALL[:4] for sp in (0, 3)] + [(n, 0) for n in CONFIG_NAMES] + [
+    (synth.Config("f_wide_table", 3, 2, 16, 2, 128, 64, (300, 5000), 6, 2, seed=401, max_pages=1500), 0),
+    (synth.Config("f_mp1024", 2, 4, 32, 4, 64, 64, (900, 60000), 8, 1, seed=402, invalid_frac=0.1), 2),
+]
+
+
+@pytest.mark.parametrize("cfg,splits", FUSED_CASES,
+                         ids=lambda v: v if isinstance(v, (str, int)) else v.name)
+def test_fused_select_decode_equals_composed(cfg, splits):
+    """qsa_select_sparse_decode (selection in the attention launch; two launches past 1024
+    table columns) writes the oracle's rows and, bit for bit, the composed calls' outputs."""
+    w = workload(cfg)
+    print(f"[fused select+decode] {w.cfg.name} MP={w.MP} splits={splits}", flush=True)
+    b = DeviceBatch.upload(w)
+    ref = Step(b, num_splits=splits, fused=False)
+    ref()
+    fus = Step(b, num_splits=splits, fused=True)
+    fus.selected.fill_(-7)
+    fus.out.fill_(0x1234)
+    fus()
+    torch.cuda.synchronize()
+    ref_sel = oracle.select_w(w, oracle.index_scores(w))
+    assert np.array_equal(ref.selected.cpu().numpy(), ref_sel)
+    assert np.array_equal(fus.selected.cpu().numpy(), ref_sel)
+    assert torch.equal(fus.out, ref.out)
+    assert torch.equal(fus.lse, ref.lse)
+    assert int(b.error_word[0].item()) == 0
+
+
 SAMPLES = 24
 
 
