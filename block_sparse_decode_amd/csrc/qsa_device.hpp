@@ -124,42 +124,20 @@ __device__ __forceinline__ float sum_across_groups(float v)
     return v;
 }
 
-// Block-wide exclusive prefix sum of one uint32 per thread (blockDim.x = NT, a multiple
-// of 64). `tmp` holds NT / 64 + 1 words of LDS. Returns the exclusive prefix; *total gets
-// the block sum. Contains __syncthreads().
-// Inclusive prefix sum over the 64 lanes of a wave (all lanes active).
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), on DPP lane moves:
+// a sliding sum of 4 lanes (row_shr 1, 2, 3), then row_shr 4 and 8 within each 16-lane row,
+// then row_bcast 15 and 31 carry the row totals forward. Lanes outside a move add 0.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *tmp, uint32_t *total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t x = wave_inclusive_scan(v);
-    if (lane == 63) tmp[wave] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t acc = 0;
-        for (int w = 0; w < NT / 64; ++w) {
-            uint32_t t = tmp[w];
-            tmp[w] = acc;
-            acc += t;
-        }
-        tmp[NT / 64] = acc;
-    }
-    __syncthreads();
-    uint32_t res = tmp[wave] + x - v;
-    *total = tmp[NT / 64];
-    __syncthreads();
-    return res;
+    uint32_t y = x;
+    y += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    y += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    y += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x113, 0xF, 0xF, true);   // row_shr:3
+    y += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, 0x114, 0xF, 0xE, true);   // row_shr:4, lanes 4..15
+    y += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, 0x118, 0xF, 0xC, true);   // row_shr:8, lanes 8..15
+    y += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, 0x142, 0xA, 0xF, true);   // row_bcast:15, rows 1, 3
+    y += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y, 0x143, 0xC, 0xF, true);   // row_bcast:31, rows 2, 3
+    return y;
 }
 
 }  // namespace qsa

@@ -10,7 +10,7 @@
 //  1. Non-candidates get key 0 (every candidate key is >= 0x00800000).
 //  2. The k-th largest key T is found bit by bit, most significant first: a bit is kept
 //     when at least k keys are >= the prefix with that bit set. Each count is a ballot per
-//     register slot and a scalar popcount, so it does not depend on any schedule.
+//     register slot and a scalar popcount, exact in any order.
 //  3. Keys above T are all taken. Of the keys equal to T, the highest page indices fill
 //     the remaining slots, ranked by a wave suffix count of ties.
 //  4. The union with the window is compacted in ascending page order by a wave prefix
@@ -21,6 +21,25 @@
 #include "qsa_device.hpp"
 
 namespace qsa {
+
+// Keys of the whole wave at or above t (wave-uniform): one ballot per register slot, all
+// compares of a group of 8 slots issued before the first scalar popcount reads a mask, so
+// their vector-to-scalar latencies overlap instead of adding up.
+template <int C>
+__device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[C], uint32_t t)
+{
+    uint32_t c = 0;
+#pragma unroll
+    for (int g = 0; g < C; g += 8) {
+        uint64_t m[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = __ballot(key[g + i] >= t);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c += (uint32_t)__builtin_popcountll(m[i]);
+    }
+    return c;
+}
 
 // srow: the row's MP scores; n: the row's visible pages; dst: the row's k + W output slots.
 // COHERENT: the scores were written by other workgroups of the same launch, so they are
@@ -52,14 +71,13 @@ __device__ __forceinline__ void select_row(const float *srow, int MP, int n, int
 #pragma unroll
         for (int i = 0; i < C; ++i) key[i] = c0 + i < MP ? __float_as_uint(srow[c0 + i]) : 0u;
     }
-    uint32_t ncand = 0;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int p = c0 + i;
         const float s = __uint_as_float(key[i]);
         key[i] = (p < wlo && !(s != s) && s != -__builtin_inff()) ? float_order_key(s) : 0u;
-        ncand += (uint32_t)__builtin_popcountll(__ballot(key[i] != 0u));
     }
+    const uint32_t ncand = wave_count_ge<C>(key, 1u);
 
     // 2. the k-th largest key T; keys above T are all taken, and krem of the keys equal
     //    to T (with krem = 0 no tie rule applies)
@@ -73,14 +91,9 @@ __device__ __forceinline__ void select_row(const float *srow, int MP, int n, int
         T = 0u;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t t = T | (1u << bit);
-            uint32_t cnt = 0;
-#pragma unroll
-            for (int i = 0; i < C; ++i) cnt += (uint32_t)__builtin_popcountll(__ballot(key[i] >= t));
-            if (cnt >= k) T = t;
+            if (wave_count_ge<C>(key, t) >= k) T = t;
         }
-        uint32_t ngt = 0;
-#pragma unroll
-        for (int i = 0; i < C; ++i) ngt += (uint32_t)__builtin_popcountll(__ballot(key[i] > T));
+        const uint32_t ngt = wave_count_ge<C>(key, T + 1u);   // T < 2^32 - 1: T is a finite score's key
         krem = k - ngt;                   // >= 1
     }
 
@@ -90,7 +103,7 @@ __device__ __forceinline__ void select_row(const float *srow, int MP, int n, int
 #pragma unroll
     for (int i = 0; i < C; ++i) eq_lane += (krem != 0u && key[i] == T) ? 1u : 0u;
     const uint32_t eq_incl = wave_inclusive_scan(eq_lane);
-    uint32_t higher = (uint32_t)__shfl((int)eq_incl, 63, 64) - eq_incl;
+    uint32_t higher = (uint32_t)__builtin_amdgcn_readlane((int)eq_incl, 63) - eq_incl;
     uint64_t take = 0;                    // bit i: column c0 + i is in the row's selection
 #pragma unroll
     for (int i = C - 1; i >= 0; --i) {
@@ -107,7 +120,7 @@ __device__ __forceinline__ void select_row(const float *srow, int MP, int n, int
     // 4. ascending compaction, then -1 padding
     const uint32_t cnt_lane = (uint32_t)__builtin_popcountll(take);
     const uint32_t incl = wave_inclusive_scan(cnt_lane);
-    const uint32_t total = (uint32_t)__shfl((int)incl, 63, 64);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
     uint32_t pos = incl - cnt_lane;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
