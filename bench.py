@@ -2,8 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mtp_verify_32k]
 
-A step runs the whole path over one batch on one GPU:
-index scores -> canonical top-k -> split-KV attention (with its merge).
+A step runs the whole path over one batch on one GPU in two launches:
+index scores, then the canonical top-k fused into the split-KV attention launch
+(qsa_select_sparse_decode).
 
 Inputs are synthetic and seeded (module `synth`), already resident in HBM. The paged
 cache is replicated over several "layers", and consecutive steps walk through them,
@@ -12,10 +13,12 @@ from HBM, not from the 256 MB MALL (the pages a step touches are evicted before 
 layer comes round again).
 
 Output: one JSON line with the contract's fields plus
-  roofline      -- the dominant kernel (qsa_sparse_decode) against MI355X's 8 TB/s HBM peak,
-                   from algorithmic bytes per launch and HIP-event durations on its stream;
+  roofline      -- the dominant kernel (the fused selection + attention launch) against
+                   MI355X's 8 TB/s HBM peak, from algorithmic bytes per launch and HIP-event
+                   durations on its stream;
   cpu_baseline  -- the CPU oracle on a bounded sample of the same workload (single thread);
-  stages        -- mean HIP-event microseconds of each of the three calls.
+  stages        -- mean HIP-event microseconds of each call, the fused one and the separate
+                   selection and attention calls.
 """
 import argparse
 import json
@@ -47,7 +50,7 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def traffic_from_counters(fetch_csv, write_csv, workload):
+def traffic_from_counters(fetch_csv, write_csv, workload, kernel):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of this
     script with --copy-calibration into HBM bytes per sparse_decode_kernel launch.
 
@@ -60,9 +63,9 @@ def traffic_from_counters(fetch_csv, write_csv, workload):
 
     def load(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        dec = [float(r["Counter_Value"]) for r in rows if "sparse_decode_kernel" in r["Kernel_Name"]]
+        dec = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
         cpy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
-        assert dec, f"no sparse_decode_kernel dispatch in {path}"
+        assert dec, f"no {kernel} dispatch in {path}"
         return statistics.median(dec), cpy, len(dec)
 
     f_dec, f_cpy, n_f = load(fetch_csv, "FETCH_SIZE")
@@ -70,7 +73,7 @@ def traffic_from_counters(fetch_csv, write_csv, workload):
     f_scale = COPY_BYTES / (f_cpy * 1024.0)
     w_scale = COPY_BYTES / (w_cpy * 1024.0)
     out = {
-        "kernel": "sparse_decode_kernel", "workload": workload, "source_sha256": kernel_source_hash(),
+        "kernel": kernel, "workload": workload, "source_sha256": kernel_source_hash(),
         "fetch_kib_per_dispatch_median": f_dec, "write_kib_per_dispatch_median": w_dec,
         "dispatches": [n_f, n_w],
         "copy_fetch_kib": f_cpy, "copy_write_kib": w_cpy, "fetch_scale": f_scale, "write_scale": w_scale,
@@ -102,6 +105,8 @@ def algorithmic_bytes(w, selected):
     attention: for each request and KV head, every distinct valid page that any of its rows
     selected, K + V codes and scales (P * (d/2 + d/16) * 2 bytes); plus q, out, lse, the
     selection rows and the page-table entries it reads.
+    select_attention: the fused launch; attention plus the score table it reads (the
+    selection rows are then written instead of read).
     index:     every candidate page's key for every KV head, q, and the score table written.
     select:    the score table read and the selection written.
     """
@@ -135,8 +140,17 @@ def algorithmic_bytes(w, selected):
     attn = attn_kv + qo + qo + w.N * Hq * 4 + w.N * KW * 4 + pt_entries * 4
     index = index_keys + qo + w.N * w.MP * 4
     select = w.N * w.MP * 4 + w.N * KW * 4
-    return dict(attention=attn, attention_kv=attn_kv, index=index, select=select,
-                step=attn + index + select)
+    fused = attn + w.N * w.MP * 4
+    return dict(attention=attn, attention_kv=attn_kv, index=index, select=select, select_attention=fused,
+                step=index + fused)
+
+
+def fused_kernel_name(w):
+    """Name rocprofv3 gives the fused selection + attention kernel for this workload."""
+    c = w.cfg
+    if w.MP > 1024:
+        return f"sparse_decode_kernel<{c.head_dim}, 0>"
+    return f"sparse_decode_kernel<{c.head_dim}, {8 if w.MP <= 512 else 16}>"
 
 
 def cpu_baseline(w, max_rows):
@@ -176,7 +190,9 @@ def main():
                     help="summarise two rocprofv3 counter runs into the traffic file and exit")
     args = ap.parse_args()
     if args.traffic_from:
-        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload)
+        import synth
+        traffic_from_counters(args.traffic_from[0], args.traffic_from[1], args.workload,
+                              fused_kernel_name(synth.generate(args.workload)))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -239,6 +255,7 @@ def main():
         b2.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b2) * 1e3 / K
+    fus_us = stage_us(lambda st: st.select_decode_call(stream))
     dec_us = stage_us(lambda st: st.decode_call(stream))
     idx_us = stage_us(lambda st: st.scores_call(stream))
     sel_us = stage_us(lambda st: st.select_call(stream))
@@ -246,7 +263,7 @@ def main():
 
     ab = algorithmic_bytes(w, sel)
     us_step = wall / K * 1e6
-    achieved = ab["attention"] / (dec_us * 1e-6) / 1e9
+    achieved = ab["select_attention"] / (fus_us * 1e-6) / 1e9
     step_gbs = ab["step"] / (us_step * 1e-6) / 1e9
 
     c = w.cfg
@@ -269,13 +286,13 @@ def main():
                    "context": c.context, "topk": c.topk, "window": c.window, "kv_cache": "nvfp4",
                    "layers_rotated": args.layers,
                    "num_splits": splits or "auto"},
-        "stages": {"index_scores_us": round(idx_us, 2), "select_topk_us": round(sel_us, 2),
-                   "sparse_decode_us": round(dec_us, 2),
+        "stages": {"index_scores_us": round(idx_us, 2), "select_sparse_decode_us": round(fus_us, 2),
+                   "separate_select_topk_us": round(sel_us, 2), "separate_sparse_decode_us": round(dec_us, 2),
                    "timing": "mean of back-to-back launches between one HIP event pair on the launch stream"},
         "bytes": ab,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
-                     "kernel": "qsa_sparse_decode (sparse_decode_kernel, plus merge_splits_kernel when split)"},
+                     "kernel": "qsa_select_sparse_decode (" + fused_kernel_name(w) + ")"},
         "error_word": err,
     }
     if args.cpu_rows > 0:
