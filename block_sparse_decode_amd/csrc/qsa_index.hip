@@ -9,13 +9,12 @@
 // arithmetic must be reproducible bit for bit. It therefore runs on the plain ALUs, never
 // on MFMA, whose internal summation order is not specified. A workgroup covers 64 pages of
 // one query row; each lane owns one page and keeps that page's key for the current KV head
-// in VGPRs as fp32. Each wave takes KV heads in turn. For its KV head it stages the group's
-// q heads, 8 at a time, as fp32 in its own slice of LDS (converted once, instead of once per
-// lane and use), and every lane reads them with broadcast LDS loads. Four q heads are summed
-// at once as four independent chains, each still one fp32 fma after another in ascending
-// element order; a product of two bf16 values is exact in fp32, so the fma equals the
-// separate multiply and add. An LDS max over the waves combines the KV heads (max is exact
-// in any order).
+// in VGPRs as fp32. Each wave takes KV heads in turn. The q heads of a KV head are
+// wave-uniform: their bf16 pairs come through scalar loads and are unpacked on the scalar
+// ALU, and four q heads are summed at once as four independent chains, each still one fp32
+// fma after another in ascending element order. A product of two bf16 values is exact in
+// fp32, so the fma equals the separate multiply and add. An LDS max over the waves combines
+// the KV heads (max is exact in any order).
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
@@ -25,37 +24,36 @@ template <int D>
 __global__ __launch_bounds__(256, 3) void index_scores_kernel(IndexParams prm)
 {
     constexpr int NW = 4;
-    constexpr int QH = 8;                    // q heads staged per wave at a time
     __shared__ float red[NW][kWave];
-    __shared__ __attribute__((aligned(16))) float qs[NW][QH][D];
 
     const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
+    // Errors are reported at the end: a global atomic before the loop would keep the
+    // compiler from reading q through the scalar cache.
     const bool first = (j == 0 && tile == 0 && threadIdx.x == 0);
-    const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, first);
-    if (first && R > 0) {
-        int64_t L_b = prm.seq_lens[b];
-        if (L_b < r1 - r0 || L_b > (int64_t)prm.MP * prm.P) set_error(prm.err, QSA_DEVERR_SEQ_LEN);
+    const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, false);
+    if (j >= R) {
+        if (first) clip_rows(r0, r1, prm.N, prm.rmax, prm.err, true);
+        return;
     }
-    if (j >= R) return;
     const int row = r0 + j;
     const RowGeom geo = row_geom(prm.seq_lens[b], r1 - r0, j, prm.log2P, prm.MP);
 
     const int p = tile * kWave + lane;
     int phys = -1;
-    bool cand = false;
+    bool cand = false, bad_page = false;
     if (p < prm.MP) {
         phys = prm.page_table[(int64_t)b * prm.MP + p];
-        if (p < geo.pages && (phys < -1 || (int64_t)phys >= prm.NP)) set_error(prm.err, QSA_DEVERR_PAGE_ID);
+        bad_page = p < geo.pages && (phys < -1 || (int64_t)phys >= prm.NP);
         cand = (p < geo.pages - prm.W) && phys >= 0 && (int64_t)phys < prm.NP;
     }
     const bool any_cand = __any(cand);
 
     const int G = prm.Hq / prm.Hkv;
-    float *qw = &qs[wave][0][0];
+    const int wv = __builtin_amdgcn_readfirstlane(wave);     // wave-uniform: q comes by scalar loads
     float best = __builtin_nanf("");
-    for (int g = wave; g < prm.Hkv && any_cand; g += NW) {
+    for (int g = wv; g < prm.Hkv && any_cand; g += NW) {
         // this page's key for KV head g, as fp32 in registers
         float k[D];
         {
@@ -69,56 +67,31 @@ __global__ __launch_bounds__(256, 3) void index_scores_kernel(IndexParams prm)
                 k[8 * c + 6] = bf16lo(v.w); k[8 * c + 7] = bf16hi(v.w);
             }
         }
-        for (int hc = 0; hc < G; hc += QH) {
-            const int nh = min(QH, G - hc);
-            // stage q heads g*G + hc .. + nh of this row as fp32: lane handles QH * D / 64
-            // consecutive elements of the chunk
-            constexpr int EPL = QH * D / 64;            // elements per lane (16 or 8)
-            const int e0 = lane * EPL;
-            if (e0 < nh * D) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(
-                    prm.q32 + ((int64_t)row * prm.Hq + g * G + hc) * (D / 2) + e0 / 2);
+        // four q heads at a time, each its own sequential fp32 chain; their bf16 pairs are
+        // wave-uniform, so they arrive in scalar registers and unpack on the scalar ALU
+        for (int h4 = 0; h4 < G; h4 += 4) {
+            const int nh = min(4, G - h4);
+            const uint32_t *q0 = prm.q32 + ((int64_t)row * prm.Hq + g * G + h4) * (D / 2);
+            const uint32_t *q1 = nh > 1 ? q0 + D / 2 : q0;
+            const uint32_t *q2 = nh > 2 ? q0 + D : q0;
+            const uint32_t *q3 = nh > 3 ? q0 + 3 * (D / 2) : q0;
+            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
 #pragma unroll
-                for (int c = 0; c < EPL / 8; ++c) {
-                    const uint4 v = src[c];
-                    const float4 lo = make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
-                    const float4 hi = make_float4(bf16lo(v.z), bf16hi(v.z), bf16lo(v.w), bf16hi(v.w));
-                    *reinterpret_cast<float4 *>(qw + e0 + 8 * c) = lo;
-                    *reinterpret_cast<float4 *>(qw + e0 + 8 * c + 4) = hi;
-                }
+            for (int i = 0; i < D / 2; ++i) {
+                const uint32_t u0 = q0[i], u1 = q1[i], u2 = q2[i], u3 = q3[i];
+                a0 = __builtin_fmaf(bf16lo(u0), k[2 * i], a0);
+                a1 = __builtin_fmaf(bf16lo(u1), k[2 * i], a1);
+                a2 = __builtin_fmaf(bf16lo(u2), k[2 * i], a2);
+                a3 = __builtin_fmaf(bf16lo(u3), k[2 * i], a3);
+                a0 = __builtin_fmaf(bf16hi(u0), k[2 * i + 1], a0);
+                a1 = __builtin_fmaf(bf16hi(u1), k[2 * i + 1], a1);
+                a2 = __builtin_fmaf(bf16hi(u2), k[2 * i + 1], a2);
+                a3 = __builtin_fmaf(bf16hi(u3), k[2 * i + 1], a3);
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the wave's LDS stores are done
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            for (int h4 = 0; h4 < nh; h4 += 4) {
-                const float *q0 = qw + (h4 + 0) * D, *q1 = qw + (h4 + 1) * D;
-                const float *q2 = qw + (h4 + 2) * D, *q3 = qw + (h4 + 3) * D;
-                float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+            const float acc[4] = {a0, a1, a2, a3};
 #pragma unroll
-                for (int i = 0; i < D; i += 4) {
-                    const float4 x0 = *reinterpret_cast<const float4 *>(q0 + i);
-                    const float4 x1 = *reinterpret_cast<const float4 *>(q1 + i);
-                    const float4 x2 = *reinterpret_cast<const float4 *>(q2 + i);
-                    const float4 x3 = *reinterpret_cast<const float4 *>(q3 + i);
-                    a0 = __builtin_fmaf(x0.x, k[i], a0); a1 = __builtin_fmaf(x1.x, k[i], a1);
-                    a2 = __builtin_fmaf(x2.x, k[i], a2); a3 = __builtin_fmaf(x3.x, k[i], a3);
-                    a0 = __builtin_fmaf(x0.y, k[i + 1], a0); a1 = __builtin_fmaf(x1.y, k[i + 1], a1);
-                    a2 = __builtin_fmaf(x2.y, k[i + 1], a2); a3 = __builtin_fmaf(x3.y, k[i + 1], a3);
-                    a0 = __builtin_fmaf(x0.z, k[i + 2], a0); a1 = __builtin_fmaf(x1.z, k[i + 2], a1);
-                    a2 = __builtin_fmaf(x2.z, k[i + 2], a2); a3 = __builtin_fmaf(x3.z, k[i + 2], a3);
-                    a0 = __builtin_fmaf(x0.w, k[i + 3], a0); a1 = __builtin_fmaf(x1.w, k[i + 3], a1);
-                    a2 = __builtin_fmaf(x2.w, k[i + 3], a2); a3 = __builtin_fmaf(x3.w, k[i + 3], a3);
-                }
-                const float acc[4] = {a0, a1, a2, a3};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    if (h4 + t >= nh) break;
-                    if (!(acc[t] != acc[t]) && ((best != best) || acc[t] > best)) best = acc[t];
-                }
-            }
-            // the next chunk overwrites this wave's slice: every lane has read it
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_wave_barrier();
+            for (int t = 0; t < 4; ++t)
+                if (t < nh && !(acc[t] != acc[t]) && ((best != best) || acc[t] > best)) best = acc[t];
         }
     }
     red[wave][lane] = best;
@@ -133,6 +106,12 @@ __global__ __launch_bounds__(256, 3) void index_scores_kernel(IndexParams prm)
         float s = prm.sm_scale * m;
         if (s == 0.0f) s = 0.0f;                 // store +0 for either zero
         prm.scores[(int64_t)row * prm.MP + p] = cand ? s : -__builtin_inff();
+    }
+    if (bad_page) set_error(prm.err, QSA_DEVERR_PAGE_ID);
+    if (first) {
+        clip_rows(r0, r1, prm.N, prm.rmax, prm.err, true);
+        const int64_t L_b = prm.seq_lens[b];
+        if (L_b < r1 - r0 || L_b > (int64_t)prm.MP * prm.P) set_error(prm.err, QSA_DEVERR_SEQ_LEN);
     }
 }
 
