@@ -127,8 +127,28 @@ class Step:
         self.lse = batch.new_lse() if with_lse else None
         self.ws = batch.new_workspace(num_splits)
 
+        # the raw argument lists of the two calls of a step, built once (pointers of the
+        # tensors above); a step then costs two foreign calls
+        import ctypes
+        from . import QsaError, lib
+        self._L = lib()
+        self._QsaError = QsaError
+        sh, pg = ctypes.byref(self.shape_), ctypes.byref(self.paged_)
+        ws = self.ws
+        self._a_scores = (sh, pg, self.b.q.data_ptr(), self.scores.data_ptr())
+        self._a_fused = (sh, pg, self.b.q.data_ptr(), self.scores.data_ptr(), self.selected.data_ptr(),
+                         self.out.data_ptr(), None if self.lse is None else self.lse.data_ptr(), int(num_splits),
+                         ws.data_ptr(), ws.numel())
+
+    def _raw(self, fn, args, stream, name):
+        import torch
+        st = (torch.cuda.current_stream() if stream is None else stream).cuda_stream
+        status = fn(*args, st)
+        if status != 0:
+            raise self._QsaError(status, name)
+
     def scores_call(self, stream=None):
-        qsa_index_scores(self.shape_, self.paged_, self.b.q, self.scores, stream)
+        self._raw(self._L.qsa_index_scores, self._a_scores, stream, "qsa_index_scores")
 
     def select_call(self, stream=None):
         qsa_select_topk(self.shape_, self.paged_, self.scores, self.selected, stream)
@@ -138,8 +158,7 @@ class Step:
                           self.out, self.lse, self.num_splits, self.ws, None, stream)
 
     def select_decode_call(self, stream=None):
-        qsa_select_sparse_decode(self.shape_, self.paged_, self.b.q, self.scores, self.selected, self.out, self.lse,
-                                 self.num_splits, self.ws, None, stream)
+        self._raw(self._L.qsa_select_sparse_decode, self._a_fused, stream, "qsa_select_sparse_decode")
 
     def __call__(self, stream=None):
         self.scores_call(stream)
