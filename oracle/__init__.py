@@ -17,6 +17,8 @@ Parity status (see tests/test_oracle_*.py):
   selection            pinned: brute force over all tie patterns, invariants
   attention            pinned: brute-force dense softmax, torch SDPA (fp64) on full windows,
                        single-token and equal-key closed forms
+  KV store             pinned: brute-force nearest-code search over every E2M1 / E4M3 code,
+                       exactly representable blocks, closed-form index keys
 """
 from __future__ import annotations
 
@@ -77,6 +79,12 @@ def _declare(L):
                                    _P, _P, _P, _P, _P, _P, _I, _P, _P]
     L.oracle_attention_one.argtypes = [_I, _P, _P, _P, _I, _I64, _I, _I, _I, _I, _F, _D, _D,
                                        _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P]
+    L.oracle_e4m3_encode.argtypes = [_F]
+    L.oracle_e4m3_encode.restype = ctypes.c_uint8
+    L.oracle_e2m1_encode.argtypes = [_F]
+    L.oracle_e2m1_encode.restype = ctypes.c_uint8
+    L.oracle_nvfp4_encode_block.argtypes = [_P, _F, _P, _P]
+    L.oracle_kv_store.argtypes = [_I, _P, _P, _P, _I, _I64, _I, _I, _I, _F, _F, _P, _P, _P, _P, _P, _P, _P]
 
 
 def _c(a, dtype):
@@ -198,3 +206,41 @@ def attention_one(w, selected, row, head, sm_scale=None):
                                sel.shape[1], int(row), int(head), out.ctypes.data_as(_P),
                                lse.ctypes.data_as(_P))
     return out, float(lse[0])
+
+
+def e4m3_encode(t: float) -> int:
+    """The E4M3 code nearest to a non-negative fp32 value (ties to the even code, at most 448)."""
+    return int(lib().oracle_e4m3_encode(float(t)))
+
+
+def e2m1_encode(y: float) -> int:
+    """The E2M1 code nearest to an fp32 value (ties to the even code, magnitude at most 6)."""
+    return int(lib().oracle_e2m1_encode(float(y)))
+
+
+def nvfp4_encode_block(x, global_scale=1.0):
+    """One block of 16 fp32 values -> (8 code bytes, scale byte)."""
+    x, xp = _c(np.asarray(x, np.float32).reshape(16), np.float32)
+    codes = np.zeros(8, np.uint8)
+    sc = np.zeros(1, np.uint8)
+    lib().oracle_nvfp4_encode_block(xp, float(global_scale), codes.ctypes.data_as(_P), sc.ctypes.data_as(_P))
+    return codes, int(sc[0])
+
+
+def kv_store(w, new_k, new_v):
+    """The KV store of one step on copies of the workload's planes.
+
+    new_k / new_v: bf16 bits [N][Hkv][d]. Returns (k_codes, k_scales, v_codes, v_scales,
+    index_keys) after the store; the workload itself is not modified.
+    """
+    c = w.cfg
+    sl, slp = _c(w.seq_lens, np.int32)
+    ro, rop = _c(w.row_offsets, np.int32)
+    pt, ptp = _c(w.page_table, np.int32)
+    nk, nkp = _c(new_k, np.uint16)
+    nv, nvp = _c(new_v, np.uint16)
+    planes = [np.array(a, copy=True) for a in (w.k_codes, w.k_scales, w.v_codes, w.v_scales, w.index_keys)]
+    ptrs = [a.ctypes.data_as(_P) for a in planes]
+    lib().oracle_kv_store(w.B, slp, rop, ptp, w.MP, w.NP, c.kv_heads, c.page_size, c.head_dim,
+                          float(c.k_global), float(c.v_global), nkp, nvp, *ptrs)
+    return tuple(planes)

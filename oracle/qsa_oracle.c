@@ -370,3 +370,129 @@ void oracle_attention_one(int B, const int32_t *seq_lens, const int32_t *row_off
     free(o);
     free(ls);
 }
+
+/* ------------------------------------------------------------- KV store -- */
+/*
+ * The KV-store prologue of a decode / verify step [PR20276, Performance > What runs on
+ * the fast paths: the decode prologue covers index store and compression; PR20937, What
+ * changes: a fused decode prologue over NVFP4 KV]: this step's new K and V tokens are
+ * quantised into their page slots, and the index key of every page that received a token
+ * is recomputed. The pages fix neither the encoder's rounding nor the index compression;
+ * this file takes these readings:
+ *
+ *   placement  row j of request b (R rows, L = seq_lens[b] tokens including the new ones)
+ *              is the token at position pos = L - R + j, page pos / P, slot pos % P, in
+ *              physical page page_table[b][pos / P] (skipped if that entry is not valid);
+ *   scale      per block of 16 consecutive elements x (bf16 inputs, exact in fp32):
+ *              amax = max |x|; t = fl32(fl32(amax / 6) / global); scale = the E4M3 code
+ *              nearest to t (ties to the even code), at most 448 (code 0x7E);
+ *   codes      with s = e4m3(scale) * global (fp32): c = the E2M1 code nearest to
+ *              fl32(x / s) (ties to the even code), magnitude at most 6; all codes 0 when
+ *              s == 0;
+ *   index key  for each KV head and element i: bf16_RNE(fl32(S_i / n)), S_i the fp32 sum,
+ *              in ascending token order, of the page's stored K (dequantised, exact in
+ *              fp32) over its n = min(P, L - page * P) valid tokens.
+ */
+
+/* nearest code of a non-negative value among `n` increasing grid values (ties to the even code) */
+static int nearest_even(double y, const double *grid, int n)
+{
+    int best = 0;
+    for (int c = 1; c < n; ++c) {
+        const double dc = fabs(y - grid[c]), db = fabs(y - grid[best]);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    return best;
+}
+
+uint8_t oracle_e4m3_encode(float t)
+{
+    /* t >= 0; the 127 finite non-negative codes 0x00..0x7E in increasing order */
+    double grid[127];
+    for (int c = 0; c < 127; ++c) grid[c] = oracle_e4m3(c);
+    if (t >= 448.0f) return 0x7E;
+    return (uint8_t)nearest_even((double)t, grid, 127);
+}
+
+uint8_t oracle_e2m1_encode(float y)
+{
+    double grid[8];
+    for (int c = 0; c < 8; ++c) grid[c] = oracle_e2m1(c);
+    const int sign = y < 0.0f;
+    const double a = fabs((double)y);
+    const int mag = a >= 6.0 ? 7 : nearest_even(a, grid, 8);
+    return (uint8_t)(mag | (sign && mag ? 8 : 0));
+}
+
+/* one block of 16 elements: codes[8] (low nibble = even element) and the scale byte */
+void oracle_nvfp4_encode_block(const float *x, float global, uint8_t *codes, uint8_t *scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 16; ++i)
+        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+    const float t = (amax / 6.0f) / global;
+    const uint8_t sc = oracle_e4m3_encode(t);
+    const float s = (float)oracle_e4m3(sc) * global;
+    for (int i = 0; i < 8; ++i) {
+        uint8_t lo = 0, hi = 0;
+        if (s != 0.0f) {
+            lo = oracle_e2m1_encode(x[2 * i] / s);
+            hi = oracle_e2m1_encode(x[2 * i + 1] / s);
+        }
+        codes[i] = (uint8_t)(lo | (hi << 4));
+    }
+    *scale = sc;
+}
+
+/* The whole store: writes the new tokens' codes and scales into the planes and rewrites
+   the index keys of the pages that received a token. new_k / new_v: bf16 [N][Hkv][d]. */
+void oracle_kv_store(int B, const int32_t *seq_lens, const int32_t *row_offsets, const int32_t *page_table,
+                     int MP, int64_t NP, int Hkv, int P, int d, float k_global, float v_global,
+                     const uint16_t *new_k, const uint16_t *new_v, uint8_t *k_codes, uint8_t *k_scales,
+                     uint8_t *v_codes, uint8_t *v_scales, uint16_t *index_keys)
+{
+    for (int b = 0; b < B; ++b) {
+        const int r0 = row_offsets[b], R = row_offsets[b + 1] - r0;
+        const int64_t L = seq_lens[b];
+        for (int j = 0; j < R; ++j) {
+            const int64_t pos = L - R + j;
+            if (pos < 0 || pos / P >= MP) continue;
+            const int32_t phys = page_table[(int64_t)b * MP + pos / P];
+            if (!valid_page(phys, NP)) continue;
+            for (int h = 0; h < Hkv; ++h) {
+                const int64_t tok = ((int64_t)phys * Hkv + h) * P + pos % P;
+                for (int blk = 0; blk < d / 16; ++blk) {
+                    float xk[16], xv[16];
+                    for (int i = 0; i < 16; ++i) {
+                        xk[i] = bf16_to_f32(new_k[((int64_t)(r0 + j) * Hkv + h) * d + blk * 16 + i]);
+                        xv[i] = bf16_to_f32(new_v[((int64_t)(r0 + j) * Hkv + h) * d + blk * 16 + i]);
+                    }
+                    oracle_nvfp4_encode_block(xk, k_global, k_codes + tok * (d / 2) + blk * 8, k_scales + tok * (d / 16) + blk);
+                    oracle_nvfp4_encode_block(xv, v_global, v_codes + tok * (d / 2) + blk * 8, v_scales + tok * (d / 16) + blk);
+                }
+            }
+        }
+        /* index keys of the pages that received a token */
+        for (int j = 0; j < R; ++j) {
+            const int64_t pos = L - R + j;
+            if (pos < 0 || pos / P >= MP) continue;
+            const int64_t page = pos / P;
+            if (j > 0 && (L - R + j - 1) >= 0 && (L - R + j - 1) / P == page) continue;   /* page done already */
+            const int32_t phys = page_table[(int64_t)b * MP + page];
+            if (!valid_page(phys, NP)) continue;
+            const int64_t n = L - page * P < P ? L - page * P : P;
+            for (int h = 0; h < Hkv; ++h) {
+                for (int i = 0; i < d; ++i) {
+                    float S = 0.0f;
+                    for (int64_t t = 0; t < n; ++t) {
+                        S = S + (float)oracle_dequant_elem(k_codes, k_scales, k_global, Hkv, P, d, phys, h, (int)t, i);
+                    }
+                    const float mean = S / (float)n;
+                    uint32_t u;
+                    memcpy(&u, &mean, 4);
+                    index_keys[((int64_t)phys * Hkv + h) * d + i] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                }
+            }
+        }
+    }
+}
