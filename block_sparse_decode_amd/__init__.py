@@ -16,7 +16,7 @@ from typing import Optional
 __all__ = [
     "QsaError", "Shape", "Paged", "lib", "qsa_abi_version", "qsa_status_string",
     "qsa_index_scores", "qsa_select_topk", "qsa_workspace_bytes", "qsa_sparse_decode",
-    "qsa_select_sparse_decode", "qsa_nvfp4_dequant_pages", "LIB_PATH", "EXPORTED",
+    "qsa_select_sparse_decode", "qsa_kv_store", "qsa_nvfp4_dequant_pages", "LIB_PATH", "EXPORTED",
     "QSA_DEVERR_PAGE_ID", "QSA_DEVERR_SEQ_LEN", "QSA_DEVERR_ROWS", "QSA_DEVERR_Q_RANGE",
     "QSA_DEVERR_SELECTED",
 ]
@@ -34,7 +34,7 @@ QSA_DEVERR_SELECTED = 0x10
 # every symbol that include/qsa.h declares
 EXPORTED = (
     "qsa_index_scores", "qsa_select_topk", "qsa_workspace_bytes", "qsa_sparse_decode", "qsa_select_sparse_decode",
-    "qsa_nvfp4_dequant_pages", "qsa_status_string", "qsa_abi_version",
+    "qsa_kv_store", "qsa_nvfp4_dequant_pages", "qsa_status_string", "qsa_abi_version",
 )
 
 
@@ -99,12 +99,13 @@ def lib() -> ctypes.CDLL:
         L.qsa_workspace_bytes.restype = SZ
         L.qsa_sparse_decode.argtypes = [sp, pp, P, P, P, P, I32, P, SZ, P]
         L.qsa_select_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, I32, P, SZ, P]
+        L.qsa_kv_store.argtypes = [sp, pp, P, P, P]
         L.qsa_nvfp4_dequant_pages.argtypes = [sp, P, P, ctypes.c_float, P, I32, P, P]
         L.qsa_status_string.argtypes = [ctypes.c_int]
         L.qsa_status_string.restype = ctypes.c_char_p
         L.qsa_abi_version.restype = I32
         for name in ("qsa_index_scores", "qsa_select_topk", "qsa_sparse_decode", "qsa_select_sparse_decode",
-                     "qsa_nvfp4_dequant_pages"):
+                     "qsa_kv_store", "qsa_nvfp4_dequant_pages"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -170,6 +171,11 @@ def qsa_select_sparse_decode(shape: Shape, paged: Paged, q, scores, selected, ou
     _check(lib().qsa_select_sparse_decode(ctypes.byref(shape), ctypes.byref(paged), _ptr(q), _ptr(scores),
                                           _ptr(selected), _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace),
                                           int(workspace_bytes), _stream(stream)), "qsa_select_sparse_decode")
+
+
+def qsa_kv_store(shape: Shape, paged: Paged, new_k, new_v, stream=None) -> None:
+    _check(lib().qsa_kv_store(ctypes.byref(shape), ctypes.byref(paged), _ptr(new_k), _ptr(new_v), _stream(stream)),
+           "qsa_kv_store")
 
 
 def qsa_nvfp4_dequant_pages(shape: Shape, codes, scales, global_scale: float, pages, num_pages: int, out,

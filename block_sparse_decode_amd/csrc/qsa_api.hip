@@ -314,6 +314,46 @@ qsa_status qsa_select_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, co
     return decode_call(sh, pg, q, scores, selected, out, lse, num_splits, workspace, workspace_bytes, stream);
 }
 
+qsa_status qsa_kv_store(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *new_k, const uint16_t *new_v,
+                        void *stream)
+{
+    qsa_status st = check_shape(sh);
+    if (st != QSA_OK) return st;
+    if ((st = check_rows_ptrs(pg)) != QSA_OK) return st;
+    if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
+    if (!new_k || !new_v || !pg->page_table || !pg->k_codes || !pg->k_scales || !pg->v_codes || !pg->v_scales ||
+        !pg->index_keys)
+        return QSA_ERR_INVALID_ARG;
+    if (!aligned16(new_k) || !aligned16(new_v) || !aligned16(pg->page_table) || !aligned16(pg->k_codes) ||
+        !aligned16(pg->k_scales) || !aligned16(pg->v_codes) || !aligned16(pg->v_scales) || !aligned16(pg->index_keys))
+        return QSA_ERR_INVALID_ARG;
+    if (!isfinite(pg->k_global) || !isfinite(pg->v_global) || !(pg->k_global > 0.0f) || !(pg->v_global > 0.0f))
+        return QSA_ERR_INVALID_ARG;
+    StoreParams prm;
+    prm.page_table = pg->page_table;
+    prm.seq_lens = pg->seq_lens;
+    prm.row_offsets = pg->row_offsets;
+    prm.new_k = new_k;
+    prm.new_v = new_v;
+    // the planes are written through the same pointers the other calls read
+    prm.k_codes = const_cast<uint8_t *>(pg->k_codes);
+    prm.k_scales = const_cast<uint8_t *>(pg->k_scales);
+    prm.v_codes = const_cast<uint8_t *>(pg->v_codes);
+    prm.v_scales = const_cast<uint8_t *>(pg->v_scales);
+    prm.index_keys = const_cast<uint16_t *>(pg->index_keys);
+    prm.err = pg->error_word;
+    prm.NP = sh->num_phys_pages;
+    prm.N = sh->num_rows;
+    prm.MP = sh->max_pages;
+    prm.P = sh->page_size;
+    prm.Hkv = sh->num_kv_heads;
+    prm.rmax = sh->max_rows_per_request;
+    prm.k_global = pg->k_global;
+    prm.v_global = pg->v_global;
+    hipError_t e = launch_kv_store(prm, sh->head_dim, sh->num_requests, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
 qsa_status qsa_nvfp4_dequant_pages(const qsa_shape *sh, const uint8_t *codes, const uint8_t *scales,
                                    float global_scale, const int32_t *pages, int32_t num_pages, float *out,
                                    void *stream)

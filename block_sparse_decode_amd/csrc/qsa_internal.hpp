@@ -54,6 +54,23 @@ struct DecodeParams {
     float v_global;
 };
 
+struct StoreParams {
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    const int32_t *row_offsets;
+    const uint16_t *new_k;    // bf16 [N][Hkv][d]
+    const uint16_t *new_v;
+    uint8_t *k_codes;
+    uint8_t *k_scales;
+    uint8_t *v_codes;
+    uint8_t *v_scales;
+    uint16_t *index_keys;
+    uint32_t *err;
+    int64_t NP;
+    int N, MP, P, Hkv, rmax;
+    float k_global, v_global;
+};
+
 struct DequantParams {
     const uint8_t *codes;
     const uint8_t *scales;
@@ -71,6 +88,7 @@ hipError_t launch_sparse_decode(const DecodeParams &prm, int D, hipStream_t stre
 // prologue (MP <= 1024); `selected` is written as qsa_select_topk writes it
 hipError_t launch_select_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream);
 hipError_t launch_dequant_pages(const DequantParams &prm, int D, hipStream_t stream);
+hipError_t launch_kv_store(const StoreParams &prm, int D, int B, hipStream_t stream);
 
 // number of waves per decode workgroup
 constexpr int kDecodeWaves = 8;

@@ -184,6 +184,30 @@ qsa_status qsa_select_sparse_decode(const qsa_shape *shape, const qsa_paged *pag
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The KV-store prologue of a step (PR #20276, Performance > What runs on the fast paths:
+ * the decode prologue's index store and compression; PR #20937, What changes: a fused
+ * decode prologue over NVFP4 KV). Writes this step's new tokens into the paged cache and
+ * recomputes the index keys of the pages that received them.
+ *   new_k, new_v  bf16 [N][Hkv][d]  (device): row j of request b (R_b rows) is the token at
+ *                 position seq_lens[b] - R_b + j, i.e. page (pos / P), slot (pos % P)
+ * For each new token and KV head, per block of 16 elements x (K with k_global, V with
+ * v_global): scale = the E4M3 code nearest to fl32(fl32(amax|x| / 6) / global), ties to the
+ * even code, at most 448; code_i = the E2M1 code nearest to fl32(x_i / (e4m3(scale) *
+ * global)), ties to the even code, magnitude at most 6 (+0 when it rounds to zero; all 0 when
+ * the scale is 0). Then for each page that received a token and each KV head:
+ *   index_keys[phys][h][i] = bf16_RNE(fl32(S_i / n)),
+ * S_i the fp32 sum, in ascending token order, of the page's stored K (e2m1 * e4m3 * k_global)
+ * over its n = min(P, seq_lens[b] - page * P) valid tokens.
+ * WRITES through paged->k_codes, k_scales, v_codes, v_scales and index_keys (the caller's
+ * device memory; the const in qsa_paged is for the read-only calls). A new token whose page
+ * entry is -1 is skipped; one outside [-1, NP) is skipped and sets QSA_DEVERR_PAGE_ID;
+ * seq_lens[b] < R_b sets QSA_DEVERR_SEQ_LEN. Pages that receive tokens must not be shared
+ * between requests of one call. k_global and v_global must be positive.
+ */
+qsa_status qsa_kv_store(const qsa_shape *shape, const qsa_paged *paged,
+                        const uint16_t *new_k, const uint16_t *new_v, void *stream);
+
+/*
  * Parity hook: NVFP4 dequantisation of whole pages through the same device decode that
  * qsa_sparse_decode uses (the counterpart of the pages' NVFP4 page -> bf16 conversion,
  * PR #20937, qsa_nvfp4_pages_to_bf16).

@@ -142,6 +142,31 @@ def test_fused_select_decode_validation():
                 FAKE, q.qsa_workspace_bytes(sh, 4) - 1, None) == 3
 
 
+def test_kv_store_validation():
+    sh, pg = _shape(), _paged()
+    args = lambda s, p, k=FAKE, v=FAKE: (ctypes.byref(s), ctypes.byref(p), k, v, None)
+    # the new tokens and every plane the store writes are required, 16-byte aligned
+    assert _raw("qsa_kv_store", *args(sh, pg, k=None)) == 1
+    assert _raw("qsa_kv_store", *args(sh, pg, v=None)) == 1
+    assert _raw("qsa_kv_store", *args(sh, pg, k=FAKE + 2)) == 1
+    for plane in ("page_table", "k_codes", "k_scales", "v_codes", "v_scales", "index_keys"):
+        assert _raw("qsa_kv_store", *args(sh, _paged(**{plane: None}))) == 1, plane
+        assert _raw("qsa_kv_store", *args(sh, _paged(**{plane: FAKE + 8}))) == 1, plane
+    # global scales: positive and finite
+    for g in (0.0, -1.0, float("nan"), float("inf")):
+        assert _raw("qsa_kv_store", *args(sh, _paged(k_global=g))) == 1
+        assert _raw("qsa_kv_store", *args(sh, _paged(v_global=g))) == 1
+    # the shape checks apply
+    assert _raw("qsa_kv_store", *args(_shape(head_dim=96), pg)) == 2
+    assert _raw("qsa_kv_store", *args(_shape(max_rows_per_request=5), pg)) == 2
+    assert _raw("qsa_kv_store", *args(_shape(num_rows=9), pg)) == 1
+    assert _raw("qsa_kv_store", None, ctypes.byref(pg), FAKE, FAKE, None) == 1
+    assert _raw("qsa_kv_store", ctypes.byref(sh), None, FAKE, FAKE, None) == 1
+    # an empty batch is a no-op, whatever the pointers
+    assert _raw("qsa_kv_store", ctypes.byref(_shape(num_requests=0, num_rows=0)), ctypes.byref(pg), None, None,
+                None) == 0
+
+
 def test_workspace_sizing():
     sh = _shape()
     assert q.qsa_workspace_bytes(sh, 1) == 0
