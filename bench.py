@@ -36,12 +36,16 @@ COPY_BYTES = 1 << 30           # the calibration copy (--copy-calibration)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_decode_{workload}.json")
 
 
+# the sources that build and launch the fused selection + attention kernel
+DECODE_SOURCES = ("qsa_api.hip", "qsa_decode.hip", "qsa_device.hpp", "qsa_internal.hpp", "qsa_select_row.hpp")
+
+
 def kernel_source_hash():
-    """SHA-256 over the HIP sources and the header; traffic counters are valid for this hash only."""
-    import glob
+    """SHA-256 over the sources of the fused kernel and the header; traffic counters are valid
+    for this hash only."""
     import hashlib
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "block_sparse_decode_amd", "csrc", "*"))) + \
+    files = [os.path.join(ROOT, "block_sparse_decode_amd", "csrc", f) for f in DECODE_SOURCES] + \
         [os.path.join(ROOT, "include", "qsa.h")]
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -143,6 +147,33 @@ def algorithmic_bytes(w, selected):
     fused = attn + w.N * w.MP * 4
     return dict(attention=attn, attention_kv=attn_kv, index=index, select=select, select_attention=fused,
                 step=index + fused)
+
+
+def store_bytes(w):
+    """Bytes the KV store must move per step: the new K and V rows read (bf16), their codes and
+    scales written, the stored K of each touched page's other valid tokens read back for the
+    key, and the keys written."""
+    c = w.cfg
+    P, d, Hkv = c.page_size, c.head_dim, c.kv_heads
+    tok = d // 2 + d // 16
+    new_in = new_out = old_k = keys = 0
+    for b in range(w.B):
+        r0, r1 = int(w.row_offsets[b]), int(w.row_offsets[b + 1])
+        R, L = r1 - r0, int(w.seq_lens[b])
+        new_in += R * Hkv * d * 2 * 2
+        pages = {}
+        for j in range(R):
+            pos = L - R + j
+            if pos < 0 or pos // P >= w.MP or w.page_table[b, pos // P] < 0:
+                continue
+            new_out += Hkv * tok * 2
+            pages.setdefault(pos // P, 0)
+            pages[pos // P] += 1
+        for page, fresh in pages.items():
+            n = min(P, L - page * P)
+            old_k += (n - fresh) * Hkv * tok
+            keys += Hkv * d * 2
+    return new_in + new_out + old_k + keys
 
 
 def fused_kernel_name(w):
@@ -259,9 +290,27 @@ def main():
     dec_us = stage_us(lambda st: st.decode_call(stream))
     idx_us = stage_us(lambda st: st.scores_call(stream))
     sel_us = stage_us(lambda st: st.select_call(stream))
+
+    # (3) the KV store that precedes a step (this step's new K / V rows into the pools); run
+    # last, since it rewrites the rows' slots and the touched pages' index keys
+    import ctypes
+    gen = np.random.default_rng(0)
+    new_kv = [torch.from_numpy(synth.bf16_bits_from_f32(
+        gen.standard_normal((w.N, w.cfg.kv_heads, w.cfg.head_dim), dtype=np.float32)).view(np.int16)).to(dev)
+        for _ in range(2)]
+    L = q.lib()
+    store_args = {id(st): (ctypes.byref(st.shape_), ctypes.byref(st.paged_), new_kv[0].data_ptr(),
+                           new_kv[1].data_ptr(), stream.cuda_stream) for st in steps}
+
+    def store(st):
+        status = L.qsa_kv_store(*store_args[id(st)])
+        if status != 0:
+            raise q.QsaError(status, "qsa_kv_store")
+    store_us = stage_us(store)
     err = int(base.error_word[0].item())
 
     ab = algorithmic_bytes(w, sel)
+    ab["kv_store"] = store_bytes(w)
     us_step = wall / K * 1e6
     achieved = ab["select_attention"] / (fus_us * 1e-6) / 1e9
     step_gbs = ab["step"] / (us_step * 1e-6) / 1e9
@@ -288,6 +337,8 @@ def main():
                    "num_splits": splits or "auto"},
         "stages": {"index_scores_us": round(idx_us, 2), "select_sparse_decode_us": round(fus_us, 2),
                    "separate_select_topk_us": round(sel_us, 2), "separate_sparse_decode_us": round(dec_us, 2),
+                   "kv_store_us": round(store_us, 2),
+                   "kv_store_gbs": round(ab["kv_store"] / (store_us * 1e-6) / 1e9, 1),
                    "timing": "mean of back-to-back launches between one HIP event pair on the launch stream"},
         "bytes": ab,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -16,12 +16,16 @@
 //   index key  per element: bf16_RNE(fl32(S / n)), S the fp32 sum in ascending token order
 //              of the page's stored K (dequantised) over its n valid tokens.
 //
-// Design: one workgroup per (request, KV head). Phase 1: one thread per 16-element block of
-// a new token (K or V): amax, scale and codes in registers, rounding by v_rndne on values
-// scaled by exact powers of two. A workgroup barrier makes the new slots visible to the
-// workgroup. Phase 2: one thread per (touched page, element) sums the page's dequantised K
-// over its valid tokens and writes the key. Contraction is off in this file so that every
-// fp32 sum and product is the rounded operation the definition states.
+// Design: one workgroup per (request, KV head); R <= 4 <= P, so the new tokens touch at
+// most two pages. Every global load is issued at the start: each thread's share of the new
+// rows (four elements of one 16-element block of K or V) and of the touched pages' stored K
+// (16-byte code loads, 4-byte scale loads, into LDS). Then four lanes per block: amax over
+// the quad by two xor shuffles, the scale, and four codes by threshold compares (the E2M1
+// midpoints, with the tie direction of each). A code pair goes to its page slot in HBM and,
+// for K, over the old slot in the LDS copy. Last, one thread per (touched page, element)
+// sums the page's dequantised K from LDS over its valid tokens and writes the key. No value
+// the kernel writes to HBM is read back. Contraction is off in this file so that every fp32
+// sum and product is the rounded operation the definition states.
 #pragma clang fp contract(off)
 
 #include "qsa_device.hpp"
@@ -53,38 +57,32 @@ __device__ __forceinline__ float e4m3_value(uint32_t byte)
     return e == 0 ? (float)m * 0.001953125f : __builtin_ldexpf(1.0f + (float)m * 0.125f, e - 7);
 }
 
-// E2M1 code nearest to an fp32 value, ties to the even code, magnitude at most 6.
+// E2M1 code nearest to an fp32 value, ties to the even code, magnitude at most 6: the
+// magnitude code counts the midpoints of the grid {0, .5, 1, 1.5, 2, 3, 4, 6} that |y| passes,
+// a midpoint counting when |y| lies above it, or on it when the code above it is even.
+// NaN gives +0.
 __device__ __forceinline__ uint32_t e2m1_encode(float y)
 {
     const float a = fabsf(y);
-    uint32_t mag;
-    if (!(a < 6.0f)) {
-        mag = 7u;
-    } else if (a < 1.0f) {
-        mag = (uint32_t)__builtin_rintf(a * 2.0f);         // 0, 1 (0.5) or 2 (1.0)
-    } else {
-        const int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;  // 0 .. 2
-        float m = __builtin_rintf(__builtin_ldexpf(a, 1 - e));          // 2 .. 4
-        int ee = e;
-        if (m == 4.0f) {
-            m = 2.0f;
-            ++ee;
-        }
-        mag = ee > 2 ? 7u : (uint32_t)((ee + 1) << 1) | (uint32_t)(m - 2.0f);
-    }
+    const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
     return mag | ((y < 0.0f && mag != 0u) ? 8u : 0u);
 }
 
-__device__ __forceinline__ float e2m1_value(uint32_t c)
-{
-    const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-    const float v = e == 0 ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
-    return (c & 8u) ? -v : v;
-}
+constexpr int kStoreMaxPage = 128;      // largest page size the store supports
+constexpr int kStorePages = 2;          // pages R <= 4 new tokens can touch when P >= 64
 
 template <int D>
 __global__ __launch_bounds__(256) void kv_store_kernel(StoreParams prm)
 {
+    constexpr int CB = D / 2, SB = D / 16;                  // code / scale bytes per token
+    constexpr int NB = D / 16;                              // blocks per token
+    // one quad of lanes per new block of K or V: 2 * R * NB quads fit the 256 lanes for the
+    // at most 4 rows per request that the host admits
+    static_assert(2 * 4 * NB * 4 <= 256, "one pass of quads covers the new blocks");
+    __shared__ __align__(16) uint8_t kc_lds[kStorePages][kStoreMaxPage * CB];
+    __shared__ __align__(16) uint8_t ks_lds[kStorePages][kStoreMaxPage * SB];
+
     const int b = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
     const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
     const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, g == 0 && tid == 0);
@@ -92,77 +90,111 @@ __global__ __launch_bounds__(256) void kv_store_kernel(StoreParams prm)
     const int Rb = r1 - r0;
     const int64_t L = prm.seq_lens[b];
     const int P = prm.P, MP = prm.MP;
-    constexpr int NB = D / 16;                              // blocks per token
+    const int64_t first_pos = L - Rb > 0 ? L - Rb : 0;
+    const int64_t last_pos = L - Rb + R - 1;
+    const int64_t p_lo = first_pos / P;
 
-    // ---- phase 1: quantise the new tokens' blocks (K then V) --------------------------
-    for (int task = tid; task < 2 * R * NB; task += blockDim.x) {
-        const bool is_v = task >= R * NB;
-        const int w = is_v ? task - R * NB : task;
-        const int j = w / NB, blk = w - j * NB;
-        const int64_t pos = L - Rb + j;
+    // this thread's quarter of one new block: K blocks of rows 0..R-1, then V blocks
+    const int task = tid >> 2, quarter = tid & 3;
+    const bool has_task = task < 2 * R * NB;                // whole quads: 2 R NB 4 <= 256
+    const bool is_v = task >= R * NB;
+    const int w = is_v ? task - R * NB : task;
+    const int j = w / NB, blk = w - j * NB;
+    const int64_t pos = L - Rb + j;
+    int32_t phys = -1;
+    uint2 raw = make_uint2(0u, 0u);
+    if (has_task) {
         if (pos >= 0 && pos / P < MP) {
-            const int32_t phys = prm.page_table[(int64_t)b * MP + pos / P];
+            phys = prm.page_table[(int64_t)b * MP + pos / P];
             if (phys >= 0 && (int64_t)phys < prm.NP) {
-                const uint16_t *src = (is_v ? prm.new_v : prm.new_k) + ((int64_t)(r0 + j) * prm.Hkv + g) * D + blk * 16;
-                const uint4 lo = *reinterpret_cast<const uint4 *>(src);
-                const uint4 hi = *reinterpret_cast<const uint4 *>(src + 8);
-                const uint32_t u[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                float x[16];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    x[2 * i] = bf16lo(u[i]);
-                    x[2 * i + 1] = bf16hi(u[i]);
-                }
-                float amax = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-                const float global = is_v ? prm.v_global : prm.k_global;
-                const uint32_t sc = e4m3_encode((amax / 6.0f) / global);
-                const float s = e4m3_value(sc) * global;
-                uint32_t w0 = 0u, w1 = 0u;
-                if (s != 0.0f) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) w0 |= e2m1_encode(x[i] / s) << (4 * i);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) w1 |= e2m1_encode(x[8 + i] / s) << (4 * i);
-                }
-                const int64_t tok = ((int64_t)phys * prm.Hkv + g) * P + pos % P;
-                uint8_t *codes = (is_v ? prm.v_codes : prm.k_codes) + tok * (D / 2) + blk * 8;
-                *reinterpret_cast<uint2 *>(codes) = make_uint2(w0, w1);
-                (is_v ? prm.v_scales : prm.k_scales)[tok * (D / 16) + blk] = (uint8_t)sc;
-            } else if (phys != -1) {
-                set_error(prm.err, QSA_DEVERR_PAGE_ID);
+                const uint16_t *src = (is_v ? prm.new_v : prm.new_k) + ((int64_t)(r0 + j) * prm.Hkv + g) * D +
+                                      blk * 16 + quarter * 4;
+                raw = *reinterpret_cast<const uint2 *>(src);
+            } else {
+                if (phys != -1 && quarter == 0) set_error(prm.err, QSA_DEVERR_PAGE_ID);
+                phys = -1;
             }
-        } else if (g == 0 && blk == 0 && !is_v) {
+        } else if (g == 0 && blk == 0 && !is_v && quarter == 0) {
             set_error(prm.err, QSA_DEVERR_SEQ_LEN);
         }
     }
-    __syncthreads();               // the new slots are visible to the whole workgroup
 
-    // ---- phase 2: index keys of the touched pages --------------------------------------
-    const int64_t first_pos = L - Rb > 0 ? L - Rb : 0;
-    const int64_t last_pos = L - Rb + R - 1;
-    if (last_pos < 0) return;
-    const int64_t p_lo = first_pos / P, p_hi = last_pos / P;      // at most 2 pages for R <= 4 <= P
-    for (int task = tid; task < (int)(p_hi - p_lo + 1) * D; task += blockDim.x) {
-        const int64_t page = p_lo + task / D;
-        const int i = task % D;
-        if (page >= MP) continue;
-        const int32_t phys = prm.page_table[(int64_t)b * MP + page];
-        if (phys < 0 || (int64_t)phys >= prm.NP) continue;
-        const int64_t n = L - page * P < P ? L - page * P : P;
-        const int64_t head = (int64_t)phys * prm.Hkv + g;
+    // the touched pages: physical id (or -1 when the key is not rewritten) and valid tokens
+    int32_t phys_pg[kStorePages];
+    int n_pg[kStorePages];
+#pragma unroll
+    for (int k = 0; k < kStorePages; ++k) {
+        const int64_t page = p_lo + k;
+        phys_pg[k] = -1;
+        n_pg[k] = 0;
+        if (last_pos >= 0 && page * P <= last_pos && page < MP) {
+            const int32_t ph = prm.page_table[(int64_t)b * MP + page];
+            if (ph >= 0 && (int64_t)ph < prm.NP) {
+                phys_pg[k] = ph;
+                n_pg[k] = (int)(L - page * P < P ? L - page * P : P);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kStorePages; ++k) {
+        if (phys_pg[k] < 0) continue;
+        const int64_t tok0 = ((int64_t)phys_pg[k] * prm.Hkv + g) * P;
+        const uint4 *cs = reinterpret_cast<const uint4 *>(prm.k_codes + tok0 * CB);
+        uint4 *cd = reinterpret_cast<uint4 *>(kc_lds[k]);
+        for (int x = tid; x < n_pg[k] * (CB / 16); x += blockDim.x) cd[x] = cs[x];
+        const uint32_t *ss = reinterpret_cast<const uint32_t *>(prm.k_scales + tok0 * SB);
+        uint32_t *sd = reinterpret_cast<uint32_t *>(ks_lds[k]);
+        for (int x = tid; x < n_pg[k] * (SB / 4); x += blockDim.x) sd[x] = ss[x];
+    }
+
+    // ---- quantise: amax over the quad, scale, four codes -------------------------------
+    const float x0 = bf16lo(raw.x), x1 = bf16hi(raw.x), x2 = bf16lo(raw.y), x3 = bf16hi(raw.y);
+    float amax = fmaxf(fmaxf(fabsf(x0), fabsf(x1)), fmaxf(fabsf(x2), fabsf(x3)));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const float global = is_v ? prm.v_global : prm.k_global;
+    const uint32_t sc = e4m3_encode((amax / 6.0f) / global);
+    const float s = e4m3_value(sc) * global;
+    uint32_t pair = 0u;                                     // four nibbles, element 4q in the lowest
+    if (s != 0.0f)
+        pair = e2m1_encode(x0 / s) | (e2m1_encode(x1 / s) << 4) | (e2m1_encode(x2 / s) << 8) |
+               (e2m1_encode(x3 / s) << 12);
+    __syncthreads();                                        // the LDS copy of the stored K is whole
+
+    if (phys >= 0) {
+        const int slot = (int)(pos % P);
+        const int64_t tok = ((int64_t)phys * prm.Hkv + g) * P + slot;
+        uint8_t *codes = (is_v ? prm.v_codes : prm.k_codes) + tok * CB + blk * 8 + quarter * 2;
+        *reinterpret_cast<uint16_t *>(codes) = (uint16_t)pair;
+        if (quarter == 0) (is_v ? prm.v_scales : prm.k_scales)[tok * SB + blk] = (uint8_t)sc;
+        if (!is_v) {
+            const int k = (int)(pos / P - p_lo);            // 0 or 1: pos lies in [first_pos, last_pos]
+            *reinterpret_cast<uint16_t *>(&kc_lds[k][slot * CB + blk * 8 + quarter * 2]) = (uint16_t)pair;
+            if (quarter == 0) ks_lds[k][slot * SB + blk] = (uint8_t)sc;
+        }
+    }
+    __syncthreads();
+
+    // ---- index keys of the touched pages, from LDS -------------------------------------
+    for (int t2 = tid; t2 < kStorePages * D; t2 += blockDim.x) {
+        const int k = t2 / D, i = t2 % D;
+        const int32_t ph = k == 0 ? phys_pg[0] : phys_pg[1];
+        if (ph < 0) continue;
+        const int n = k == 0 ? n_pg[0] : n_pg[1];
+        const uint8_t *cl = kc_lds[k] + i / 2;
+        const uint8_t *sl = ks_lds[k] + i / 16;
+        const int sel = i & 1;
+        const float kg = prm.k_global;
         float S = 0.0f;
-        for (int64_t t = 0; t < n; ++t) {
-            const int64_t tok = head * P + t;
-            const uint32_t byte = prm.k_codes[tok * (D / 2) + i / 2];
-            const uint32_t c = (i & 1) ? (byte >> 4) : (byte & 15u);
-            const float v = (e2m1_value(c) * e4m3_value(prm.k_scales[tok * (D / 16) + i / 16])) * prm.k_global;
-            S = S + v;
+        for (int t = 0; t < n; ++t) {
+            // exact e2m1 and e4m3 values (hardware converts with a unit scale)
+            const float e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((uint32_t)cl[t * CB], 1.0f, 0)[sel];
+            const float sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)sl[t * SB], 1.0f, false)[0];
+            S = S + (e * sv) * kg;
         }
         const float mean = S / (float)n;
         const uint32_t u = __float_as_uint(mean);
-        prm.index_keys[head * D + i] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+        prm.index_keys[((int64_t)ph * prm.Hkv + g) * D + i] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
     }
 }
 

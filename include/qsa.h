@@ -201,8 +201,9 @@ qsa_status qsa_select_sparse_decode(const qsa_shape *shape, const qsa_paged *pag
  * WRITES through paged->k_codes, k_scales, v_codes, v_scales and index_keys (the caller's
  * device memory; the const in qsa_paged is for the read-only calls). A new token whose page
  * entry is -1 is skipped; one outside [-1, NP) is skipped and sets QSA_DEVERR_PAGE_ID;
- * seq_lens[b] < R_b sets QSA_DEVERR_SEQ_LEN. Pages that receive tokens must not be shared
- * between requests of one call. k_global and v_global must be positive.
+ * a position below 0 or at or past max_pages * P (seq_lens[b] < R_b, or too long) is skipped
+ * and sets QSA_DEVERR_SEQ_LEN. Pages that receive tokens must not be shared between requests
+ * of one call. k_global and v_global must be positive and finite (else QSA_ERR_INVALID_ARG).
  */
 qsa_status qsa_kv_store(const qsa_shape *shape, const qsa_paged *paged,
                         const uint16_t *new_k, const uint16_t *new_v, void *stream);
