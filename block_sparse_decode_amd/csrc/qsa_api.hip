@@ -1,5 +1,6 @@
 // qsa_api.hip -- the C ABI of libqsa (declared in include/qsa.h): host-side validation,
 // launch-shape choice and kernel launches. No allocation, no synchronisation, no global state.
+#include <cfloat>
 #include <math.h>
 #include <algorithm>
 #include <stddef.h>
@@ -226,6 +227,10 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
         (selected && !aligned16(selected)) || (lse && !aligned16(lse)) || (fused && !aligned16(scores)))
         return QSA_ERR_INVALID_ARG;
     if (!isfinite(pg->k_global) || !isfinite(pg->v_global)) return QSA_ERR_INVALID_ARG;
+    // the logit scale sm_scale * k_global * log2(e) must be a positive normal fp32: the
+    // kernel's lazy max compares raw logits against (max + margin) / scale
+    const double qk = (double)sh->sm_scale * (double)pg->k_global * 1.4426950408889634;
+    if (!(qk >= (double)FLT_MIN && qk <= (double)FLT_MAX)) return QSA_ERR_INVALID_ARG;
     const int splits = resolve_splits(sh, num_splits);
     const size_t need = decode_ws_bytes(sh, splits);
     if (need > 0) {
@@ -265,7 +270,7 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     prm.tile_cols = tile_cols(sh);
     if (decode_tiles(sh) * splits > (int64_t)1 << 30) return QSA_ERR_UNSUPPORTED;
     prm.tiles = (int)decode_tiles(sh);
-    prm.qk_scale_log2 = (float)((double)sh->sm_scale * (double)pg->k_global * 1.4426950408889634);
+    prm.qk_scale_log2 = (float)qk;
     prm.v_global = pg->v_global;
     hipError_t e;
     if (!fused || KW == 0) {

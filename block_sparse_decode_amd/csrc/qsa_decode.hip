@@ -29,8 +29,9 @@
 //     partials in ascending split order (so the result does not depend on which split is
 //     last), writes the output and puts the counter back to zero for the next call.
 // Workgroups are dispatched round-robin over the 8 XCDs by linear id; the id -> (tile,
-// split) map keeps a tile's splits on one XCD, so the partials the last split reads are
-// in that XCD's L2.
+// split) map gives each XCD a contiguous run of (request, KV head, column tile, split)
+// items, so a tile's splits, and the tiles of one request and KV head (whose rows share
+// their window pages and often more), run on one XCD and share its L2.
 // NVFP4 -> f16 is exact (see nvfp4_dequant8). The global scales fold into the logit scale
 // and the output.
 #include "qsa_device.hpp"
@@ -67,16 +68,19 @@ struct RawTile<64> {
     uint32_t scales;    // 1 e4m3 byte
 };
 
+// `codes` / `scales`: the sub-chunk's first token (wave-uniform); `co` / `so`: this lane's
+// byte offsets from there (token li of the M-tile, chunk gq), so each load is a uniform
+// 64-bit base plus a 32-bit lane offset with no per-load vector address arithmetic.
 template <int D>
-__device__ __forceinline__ RawTile<D> load_raw(const uint8_t *codes_tok, const uint8_t *scales_tok, int gq)
+__device__ __forceinline__ RawTile<D> load_raw(const uint8_t *codes, const uint8_t *scales, uint32_t co, uint32_t so)
 {
     RawTile<D> t;
     if constexpr (D == 128) {
-        t.codes = *reinterpret_cast<const uint4 *>(codes_tok + gq * 16);
-        t.scales = *reinterpret_cast<const uint16_t *>(scales_tok + gq * 2);
+        t.codes = *reinterpret_cast<const uint4 *>(codes + co);
+        t.scales = *reinterpret_cast<const uint16_t *>(scales + so);
     } else {
-        t.codes = *reinterpret_cast<const uint2 *>(codes_tok + gq * 8);
-        t.scales = scales_tok[gq];
+        t.codes = *reinterpret_cast<const uint2 *>(codes + co);
+        t.scales = scales[so];
     }
     return t;
 }
@@ -100,16 +104,18 @@ __device__ __forceinline__ f16x8 dequant_group(const RawTile<D> &t, f16x2 sc, in
 }
 
 template <int D>
-__device__ __forceinline__ void load_unit(const DecodeParams &prm, int phys, int g, int c, int li, int gq,
+__device__ __forceinline__ void load_unit(const DecodeParams &prm, int phys, int g, int c, uint32_t co, uint32_t so,
                                           RawTile<D> (&kr)[2], RawTile<D> (&vr)[2])
 {
-    const int64_t head = (int64_t)phys * prm.Hkv + g;
-    const int64_t tok = head * prm.P + c * 32 + li;                 // token index in the pool
+    // the sub-chunk's first token in the pool (phys, g and c are wave-uniform)
+    const int64_t tok = ((int64_t)phys * prm.Hkv + g) * prm.P + c * 32;
+    const uint8_t *kc = prm.k_codes + tok * (D / 2), *ks = prm.k_scales + tok * (D / 16);
+    const uint8_t *vc = prm.v_codes + tok * (D / 2), *vsc = prm.v_scales + tok * (D / 16);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const int64_t t = tok + mt * 16;
-        kr[mt] = load_raw<D>(prm.k_codes + t * (D / 2), prm.k_scales + t * (D / 16), gq);
-        vr[mt] = load_raw<D>(prm.v_codes + t * (D / 2), prm.v_scales + t * (D / 16), gq);
+        const uint32_t cm = co + mt * 16 * (D / 2), sm = so + mt * 16 * (D / 16);
+        kr[mt] = load_raw<D>(kc, ks, cm, sm);
+        vr[mt] = load_raw<D>(vc, vsc, cm, sm);
     }
 }
 
@@ -180,17 +186,21 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     __shared__ uint32_t scan_tmp[NT / 64 + 1];
     __shared__ f16x8 q_lds[KS][64];         // the tile's q operand, in MFMA B-operand lane order
 
+    // work item i = tile * S + split, tiles numbered (request, KV head, column tile); XCD x
+    // (the dispatcher's linear id mod 8) takes the contiguous items [x * per, (x + 1) * per)
     const int S = prm.splits;
+    const int64_t n_items = (int64_t)prm.tiles * S;
+    const int64_t per = (n_items + kXcds - 1) / kXcds;
     const int wg = blockIdx.x;
-    const int rr = wg / kXcds;
-    const int s = rr % S;
-    const int tile = (rr / S) * kXcds + (wg - rr * kXcds);
-    if (tile >= prm.tiles) return;
+    const int64_t item = (int64_t)(wg % kXcds) * per + wg / kXcds;
+    if (item >= n_items) return;
+    const int tile = (int)(item / S), s = (int)(item - (int64_t)tile * S);
     const int T = prm.col_tiles;
     const int HT = prm.Hkv * T;
     const int b = tile / HT;
     const int g = (tile - b * HT) / T, ct = tile - b * HT - g * T;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform, so in SGPRs
     const int gq = lane >> 4, li = lane & 15;
     const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
     const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, tid == 0 && s == 0 && tile == b * HT);
@@ -345,8 +355,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     }
     __syncthreads();                 // union list and q ready; the scratch area becomes V staging
     const uint32_t U = scan_tmp[0];
-    const int jbit = colv ? jc - j_lo : 31;           // the lane's bit in a page's row mask
-    const int64_t lcol = colv ? row_geom(Lb, Rb, jc, prm.log2P, MP).len : 0;
+    // The lane's bit in a page's row mask (bit 8, always set below, for a padding column) and
+    // its row's visible length, at most MP pages. A padding column has a zero q, so it sees
+    // every token: its logits are exactly 0 and its results are never written.
+    const uint32_t selbit = colv ? 1u << (jc - j_lo) : 0x100u;
+    const int64_t lfull = (int64_t)MP << prm.log2P;
+    const int lcol = colv ? (int)min(row_geom(Lb, Rb, jc, prm.log2P, MP).len, lfull) : (int)lfull;
 
     // ---- 3. online softmax over this wave's sub-chunks, the next one in flight -----
     const int lc = prm.log2P - 5;                   // log2(sub-chunks per page)
@@ -361,10 +375,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
 #pragma unroll
     for (int dt = 0; dt <= NDT; ++dt) oacc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m_col = NEG_INF;
+    float thr = NEG_INF;                            // (m_col + kLazy) / c1
     half_t *vs = &vsm[wave][0];
     const f16x8 ones = {(half_t)1.0f, (half_t)1.0f, (half_t)1.0f, (half_t)1.0f,
                         (half_t)1.0f, (half_t)1.0f, (half_t)1.0f, (half_t)1.0f};
     const int trow = 4 * gq + (li >> 2);            // transposed-read rows trow, trow + 16
+    // this lane's byte offsets inside a sub-chunk's codes and scales (token li, chunk gq)
+    const uint32_t lco = (uint32_t)(li * (D / 2) + gq * (D / 8));
+    const uint32_t lso = (uint32_t)(li * (D / 16) + gq * (D / 64));
 
     // One register set: a sub-chunk's raw codes are consumed (K into the MFMA operands, V into
     // LDS) before the next sub-chunk's loads are issued into the same registers; those loads
@@ -373,7 +391,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     auto process = [&](const UnitCursor &u, const UnitCursor &un, RawTile<D>(&kr)[2], RawTile<D>(&vr)[2]) {
         const int p = (int)(u.pm & 0xffffu);
         const uint32_t rmask = (u.pm >> 16) & 0xffu;
-        const int64_t tok0 = ((int64_t)p << prm.log2P) + u.c * 32;
 
         // S^T = K Q^T (unscaled logits)
         f32x4 sacc[2];
@@ -399,36 +416,38 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
                     dequant_group<D>(vr[mt], vsc, i);
             }
         }
-        if (un.have) load_unit<D>(prm, un.phys, g, un.c, li, gq, kr, vr);
+        if (un.have) load_unit<D>(prm, un.phys, g, un.c, lco, lso, kr, vr);
 
         // online softmax with a lazily raised column max; P stays in registers
-        int lim = 0;
-        if ((rmask >> jbit) & 1u) {
-            const int64_t vis = lcol - tok0;
-            lim = vis <= 0 ? 0 : (vis >= 32 ? 32 : (int)vis);
-        }
+        const int tok0 = (p << prm.log2P) + u.c * 32;                  // wave-uniform
+        int lim = min(max(lcol - tok0, 0), 32);                        // visible tokens of the column
+        if (((rmask | 0x100u) & selbit) == 0u) lim = 0;                // its row did not select the page
         float x[8];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) x[mt * 4 + r] = sacc[mt][r];
-        if (__any(lim > 0 && lim < 32)) {
-            // a row ends inside this sub-chunk: mask token by token
+        if (__any(lim < 32)) {
+            // a row ends inside this sub-chunk, or whole columns are masked
+            const int limq = lim - gq * 4;          // token (i / 4) * 16 + gq * 4 + (i & 3) is visible
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                if ((i / 4) * 16 + gq * 4 + (i & 3) >= lim) x[i] = NEG_INF;
-        } else if (__any(lim == 0)) {
-            // whole columns are masked (their row did not select this page, or padding)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = lim ? x[i] : NEG_INF;
+                if ((i / 4) * 16 + (i & 3) >= limq) x[i] = NEG_INF;
         }
-        const float lmx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        if (__any(lmx * c1 > m_col + kLazy)) {
+        // raise the column max only when a logit passes it by more than kLazy (log2 units):
+        // x * c1 > m_col + kLazy, i.e. x > thr with c1 > 0
+        bool over = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) over |= x[i] > thr;
+        if (__any(over)) {
+            const float lmx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                    fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             const float m_new = fmaxf(m_col, max_across_groups(lmx) * c1);
             const float alpha = (m_new == NEG_INF) ? 1.0f : __builtin_amdgcn_exp2f(m_col - m_new);
 #pragma unroll
             for (int dt = 0; dt <= NDT; ++dt) oacc[dt] *= alpha;
             m_col = m_new;
+            thr = (m_col + kLazy) / c1;
         }
         const float negm = (m_col == NEG_INF) ? NEG_INF : -m_col;
         float pr[8];
@@ -455,7 +474,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     };
 
     UnitCursor u = seek_unit(u_lo + wave, u_hi, lc, u_pm, u_phys);
-    if (u.have) load_unit<D>(prm, u.phys, g, u.c, li, gq, kr, vr);
+    if (u.have) load_unit<D>(prm, u.phys, g, u.c, lco, lso, kr, vr);
     while (u.have) {
         const UnitCursor un = seek_unit(u.u + NW, u_hi, lc, u_pm, u_phys);
         process(u, un, kr, vr);
@@ -577,8 +596,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
 template <int D, int SELC>
 static hipError_t launch_decode_d(const DecodeParams &prm, hipStream_t stream)
 {
-    const int64_t groups = (prm.tiles + kXcds - 1) / kXcds;
-    const unsigned grid = (unsigned)(groups * kXcds * prm.splits);
+    const int64_t per = ((int64_t)prm.tiles * prm.splits + kXcds - 1) / kXcds;   // work items per XCD
+    const unsigned grid = (unsigned)(per * kXcds);
     sparse_decode_kernel<D, SELC><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
     return hipGetLastError();
 }

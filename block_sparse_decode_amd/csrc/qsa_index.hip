@@ -9,28 +9,38 @@
 // arithmetic must be reproducible bit for bit. It therefore runs on the plain ALUs, never
 // on MFMA, whose internal summation order is not specified. A workgroup covers 64 pages of
 // one query row; each lane owns one page and keeps that page's key for the current KV head
-// in VGPRs as fp32. Each wave takes KV heads in turn. The q heads of a KV head are
-// wave-uniform: their bf16 pairs come through scalar loads and are unpacked on the scalar
-// ALU, and four q heads are summed at once as four independent chains, each still one fp32
-// fma after another in ascending element order. A product of two bf16 values is exact in
-// fp32, so the fma equals the separate multiply and add. An LDS max over the waves combines
-// the KV heads (max is exact in any order).
+// in VGPRs as fp32. Each wave takes KV heads in turn. The q heads of a KV head are staged
+// per wave in LDS as fp32, eight heads per element, so one broadcast read (all lanes at one
+// address) feeds eight fma chains, one per head, each still one fp32 fma after another in
+// ascending element order. A product of two bf16 values is exact in fp32, so the fma equals
+// the separate multiply and add. The loads that do not depend on each other (row offsets,
+// the request's length, the page-table entries, q) are issued together at the start. An
+// LDS max over the waves combines the KV heads (max is exact in any order).
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
 namespace qsa {
 
+constexpr int kIndexWaves = 4;
+constexpr int kHeadGroup = 8;        // q heads per pass: one LDS row of 8 fp32 per element
+
 template <int D>
-__global__ __launch_bounds__(256, 3) void index_scores_kernel(IndexParams prm)
+__global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(IndexParams prm)
 {
-    constexpr int NW = 4;
+    constexpr int NW = kIndexWaves;
+    constexpr int HG = kHeadGroup;
     __shared__ float red[NW][kWave];
+    __shared__ __align__(16) float qs[NW][D][HG];   // per wave: q[head][i] of one head group, element-major
 
     const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);     // wave-uniform
+    // independent loads first: the row range, the request's length and this lane's page
     const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
-    // Errors are reported at the end: a global atomic before the loop would keep the
-    // compiler from reading q through the scalar cache.
+    const int64_t L_b = prm.seq_lens[b];
+    const int p = tile * kWave + lane;
+    const int32_t phys = p < prm.MP ? prm.page_table[(int64_t)b * prm.MP + p] : -1;
+    // errors are reported at the end, after the loop
     const bool first = (j == 0 && tile == 0 && threadIdx.x == 0);
     const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, false);
     if (j >= R) {
@@ -38,20 +48,16 @@ __global__ __launch_bounds__(256, 3) void index_scores_kernel(IndexParams prm)
         return;
     }
     const int row = r0 + j;
-    const RowGeom geo = row_geom(prm.seq_lens[b], r1 - r0, j, prm.log2P, prm.MP);
-
-    const int p = tile * kWave + lane;
-    int phys = -1;
+    const RowGeom geo = row_geom(L_b, r1 - r0, j, prm.log2P, prm.MP);
     bool cand = false, bad_page = false;
     if (p < prm.MP) {
-        phys = prm.page_table[(int64_t)b * prm.MP + p];
         bad_page = p < geo.pages && (phys < -1 || (int64_t)phys >= prm.NP);
         cand = (p < geo.pages - prm.W) && phys >= 0 && (int64_t)phys < prm.NP;
     }
     const bool any_cand = __any(cand);
 
     const int G = prm.Hq / prm.Hkv;
-    const int wv = __builtin_amdgcn_readfirstlane(wave);     // wave-uniform: q comes by scalar loads
+    float(*qw)[HG] = qs[wv];
     float best = __builtin_nanf("");
     for (int g = wv; g < prm.Hkv && any_cand; g += NW) {
         // this page's key for KV head g, as fp32 in registers
@@ -67,31 +73,51 @@ __global__ __launch_bounds__(256, 3) void index_scores_kernel(IndexParams prm)
                 k[8 * c + 6] = bf16lo(v.w); k[8 * c + 7] = bf16hi(v.w);
             }
         }
-        // four q heads at a time, each its own sequential fp32 chain; their bf16 pairs are
-        // wave-uniform, so they arrive in scalar registers and unpack on the scalar ALU
-        for (int h4 = 0; h4 < G; h4 += 4) {
-            const int nh = min(4, G - h4);
-            const uint32_t *q0 = prm.q32 + ((int64_t)row * prm.Hq + g * G + h4) * (D / 2);
-            const uint32_t *q1 = nh > 1 ? q0 + D / 2 : q0;
-            const uint32_t *q2 = nh > 2 ? q0 + D : q0;
-            const uint32_t *q3 = nh > 3 ? q0 + 3 * (D / 2) : q0;
-            float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+        for (int h0 = 0; h0 < G; h0 += HG) {
+            const int nh = min(HG, G - h0);
+            // stage q heads h0 .. h0 + nh - 1 of KV head g: lane l writes elements 2l, 2l + 1
+            // of every head (zeros past nh)
+            if (lane < D / 2) {
+                const uint32_t *qb = prm.q32 + ((int64_t)row * prm.Hq + g * G + h0) * (D / 2) + lane;
+                float lo[HG], hi[HG];
 #pragma unroll
-            for (int i = 0; i < D / 2; ++i) {
-                const uint32_t u0 = q0[i], u1 = q1[i], u2 = q2[i], u3 = q3[i];
-                a0 = __builtin_fmaf(bf16lo(u0), k[2 * i], a0);
-                a1 = __builtin_fmaf(bf16lo(u1), k[2 * i], a1);
-                a2 = __builtin_fmaf(bf16lo(u2), k[2 * i], a2);
-                a3 = __builtin_fmaf(bf16lo(u3), k[2 * i], a3);
-                a0 = __builtin_fmaf(bf16hi(u0), k[2 * i + 1], a0);
-                a1 = __builtin_fmaf(bf16hi(u1), k[2 * i + 1], a1);
-                a2 = __builtin_fmaf(bf16hi(u2), k[2 * i + 1], a2);
-                a3 = __builtin_fmaf(bf16hi(u3), k[2 * i + 1], a3);
+                for (int t = 0; t < HG; ++t) {
+                    const uint32_t u = t < nh ? qb[t * (D / 2)] : 0u;
+                    lo[t] = bf16lo(u);
+                    hi[t] = bf16hi(u);
+                }
+                float4 *d0 = reinterpret_cast<float4 *>(qw[2 * lane]);
+                float4 *d1 = reinterpret_cast<float4 *>(qw[2 * lane + 1]);
+                d0[0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
+                d0[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
+                d1[0] = make_float4(hi[0], hi[1], hi[2], hi[3]);
+                d1[1] = make_float4(hi[4], hi[5], hi[6], hi[7]);
             }
-            const float acc[4] = {a0, a1, a2, a3};
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): this wave's q rows are in LDS
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // eight chains, one per head, each in ascending element order
+            float a[HG];
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                if (t < nh && !(acc[t] != acc[t]) && ((best != best) || acc[t] > best)) best = acc[t];
+            for (int t = 0; t < HG; ++t) a[t] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                const float4 qa = *reinterpret_cast<const float4 *>(&qw[i][0]);
+                const float4 qb2 = *reinterpret_cast<const float4 *>(&qw[i][4]);
+                a[0] = __builtin_fmaf(qa.x, k[i], a[0]);
+                a[1] = __builtin_fmaf(qa.y, k[i], a[1]);
+                a[2] = __builtin_fmaf(qa.z, k[i], a[2]);
+                a[3] = __builtin_fmaf(qa.w, k[i], a[3]);
+                a[4] = __builtin_fmaf(qb2.x, k[i], a[4]);
+                a[5] = __builtin_fmaf(qb2.y, k[i], a[5]);
+                a[6] = __builtin_fmaf(qb2.z, k[i], a[6]);
+                a[7] = __builtin_fmaf(qb2.w, k[i], a[7]);
+            }
+#pragma unroll
+            for (int t = 0; t < HG; ++t)
+                if (t < nh && !(a[t] != a[t]) && ((best != best) || a[t] > best)) best = a[t];
+            // the next group's staging overwrites qw: this wave's reads are complete
+            __builtin_amdgcn_s_waitcnt(0xc07f);
         }
     }
     red[wave][lane] = best;
@@ -110,7 +136,6 @@ __global__ __launch_bounds__(256, 3) void index_scores_kernel(IndexParams prm)
     if (bad_page) set_error(prm.err, QSA_DEVERR_PAGE_ID);
     if (first) {
         clip_rows(r0, r1, prm.N, prm.rmax, prm.err, true);
-        const int64_t L_b = prm.seq_lens[b];
         if (L_b < r1 - r0 || L_b > (int64_t)prm.MP * prm.P) set_error(prm.err, QSA_DEVERR_SEQ_LEN);
     }
 }

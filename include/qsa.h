@@ -161,7 +161,8 @@ size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
  * K_raw and V_raw are e2m1 * e4m3. An empty T gives out = 0 and lse = -inf. Each request's
  * rows share one read of the union of their selected pages. fp32 accumulation; the q and
  * P operands of the MFMA tiles are f16 (q must lie in the f16 range; see QSA_DEVERR_Q_RANGE).
- * Deterministic for a fixed num_splits.
+ * Deterministic for a fixed num_splits. sm_scale * k_global * log2(e) must be a positive
+ * normal fp32 and v_global finite; otherwise QSA_ERR_INVALID_ARG.
  */
 qsa_status qsa_sparse_decode(const qsa_shape *shape, const qsa_paged *paged,
                              const uint16_t *q, const int32_t *selected,

@@ -120,6 +120,13 @@ def test_pointer_validation():
                 1 << 30, None) == 1
     assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(k_global=float("nan"))), FAKE, FAKE,
                 FAKE, None, 0, FAKE, 1 << 30, None) == 1
+    # the logit scale sm_scale * k_global must be positive
+    for bad_sh, bad_pg in ((_shape(sm_scale=0.0), pg), (_shape(sm_scale=-0.1), pg), (sh, _paged(k_global=-1.0)),
+                           (sh, _paged(k_global=0.0))):
+        assert _raw("qsa_sparse_decode", ctypes.byref(bad_sh), ctypes.byref(bad_pg), FAKE, FAKE, FAKE, None, 0,
+                    FAKE, 1 << 30, None) == 1
+        assert _raw("qsa_select_sparse_decode", ctypes.byref(bad_sh), ctypes.byref(bad_pg), FAKE, FAKE, FAKE,
+                    FAKE, None, 0, FAKE, 1 << 30, None) == 1
     # too many q columns per request (4 rows x 32 heads per KV head)
     big = _shape(num_q_heads=128)
     assert _raw("qsa_sparse_decode", ctypes.byref(big), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
