@@ -19,6 +19,9 @@ Parity status (see tests/test_oracle_*.py):
                        single-token and equal-key closed forms
   KV store             pinned: brute-force nearest-code search over every E2M1 / E4M3 code,
                        exactly representable blocks, closed-form index keys
+  rollback (rollback.py, numpy)
+                       pinned: array indexing of the cache layouts, restore invariants,
+                       round trip, skipped and reported rows
 """
 from __future__ import annotations
 
