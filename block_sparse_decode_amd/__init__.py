@@ -17,6 +17,8 @@ __all__ = [
     "QsaError", "Shape", "Paged", "lib", "qsa_abi_version", "qsa_status_string",
     "qsa_index_scores", "qsa_select_topk", "qsa_workspace_bytes", "qsa_sparse_decode",
     "qsa_select_sparse_decode", "qsa_kv_store", "qsa_nvfp4_dequant_pages", "LIB_PATH", "EXPORTED",
+    "Plane", "qsa_rollback_stash_bytes", "qsa_rollback_gather", "qsa_rollback_restore", "qsa_step_slots",
+    "QSA_DEVERR_SLOT",
     "QSA_DEVERR_PAGE_ID", "QSA_DEVERR_SEQ_LEN", "QSA_DEVERR_ROWS", "QSA_DEVERR_Q_RANGE",
     "QSA_DEVERR_SELECTED",
 ]
@@ -30,11 +32,14 @@ QSA_DEVERR_SEQ_LEN = 0x2
 QSA_DEVERR_ROWS = 0x4
 QSA_DEVERR_Q_RANGE = 0x8
 QSA_DEVERR_SELECTED = 0x10
+QSA_DEVERR_SLOT = 0x20
+QSA_MAX_PLANES = 16
 
 # every symbol that include/qsa.h declares
 EXPORTED = (
     "qsa_index_scores", "qsa_select_topk", "qsa_workspace_bytes", "qsa_sparse_decode", "qsa_select_sparse_decode",
-    "qsa_kv_store", "qsa_nvfp4_dequant_pages", "qsa_status_string", "qsa_abi_version",
+    "qsa_kv_store", "qsa_rollback_stash_bytes", "qsa_step_slots", "qsa_rollback_gather", "qsa_rollback_restore",
+    "qsa_nvfp4_dequant_pages", "qsa_status_string", "qsa_abi_version",
 )
 
 
@@ -80,6 +85,24 @@ class Paged(ctypes.Structure):
     ]
 
 
+class Plane(ctypes.Structure):
+    """Mirror of `qsa_plane`: one plane of the rollback (a device byte array and the strides
+    that address row r of it: base + pages[r] * page_stride + within[r] * slot_stride +
+    s * seg_stride, s < nseg)."""
+    _fields_ = [
+        ("base", ctypes.c_void_p),
+        ("plane_bytes", ctypes.c_int64),
+        ("page_stride", ctypes.c_int64),
+        ("slot_stride", ctypes.c_int64),
+        ("seg_stride", ctypes.c_int64),
+        ("seg_bytes", ctypes.c_int32),
+        ("nseg", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("num_slots", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -101,11 +124,18 @@ def lib() -> ctypes.CDLL:
         L.qsa_select_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, I32, P, SZ, P]
         L.qsa_kv_store.argtypes = [sp, pp, P, P, P]
         L.qsa_nvfp4_dequant_pages.argtypes = [sp, P, P, ctypes.c_float, P, I32, P, P]
+        plp = ctypes.POINTER(Plane)
+        L.qsa_rollback_stash_bytes.argtypes = [plp, I32, I32]
+        L.qsa_rollback_stash_bytes.restype = SZ
+        L.qsa_rollback_gather.argtypes = [plp, I32, P, P, I32, P, SZ, P, P]
+        L.qsa_rollback_restore.argtypes = [plp, I32, P, P, P, I32, P, SZ, P, P]
+        L.qsa_step_slots.argtypes = [sp, pp, P, P, P]
         L.qsa_status_string.argtypes = [ctypes.c_int]
         L.qsa_status_string.restype = ctypes.c_char_p
         L.qsa_abi_version.restype = I32
         for name in ("qsa_index_scores", "qsa_select_topk", "qsa_sparse_decode", "qsa_select_sparse_decode",
-                     "qsa_kv_store", "qsa_nvfp4_dequant_pages"):
+                     "qsa_kv_store", "qsa_nvfp4_dequant_pages", "qsa_rollback_gather", "qsa_rollback_restore",
+                     "qsa_step_slots"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -183,3 +213,36 @@ def qsa_nvfp4_dequant_pages(shape: Shape, codes, scales, global_scale: float, pa
     _check(lib().qsa_nvfp4_dequant_pages(ctypes.byref(shape), _ptr(codes), _ptr(scales), float(global_scale),
                                          _ptr(pages), int(num_pages), _ptr(out), _stream(stream)),
            "qsa_nvfp4_dequant_pages")
+
+
+def _planes(planes):
+    arr = (Plane * len(planes))(*planes)
+    return arr, len(planes)
+
+
+def qsa_rollback_stash_bytes(planes, num_rows: int) -> int:
+    arr, n = _planes(planes)
+    return int(lib().qsa_rollback_stash_bytes(arr, n, int(num_rows)))
+
+
+def qsa_step_slots(shape: Shape, paged: Paged, pages, within, stream=None) -> None:
+    _check(lib().qsa_step_slots(ctypes.byref(shape), ctypes.byref(paged), _ptr(pages), _ptr(within),
+                                _stream(stream)), "qsa_step_slots")
+
+
+def qsa_rollback_gather(planes, pages, within, num_rows: int, stash, stash_bytes: Optional[int] = None,
+                        error_word=None, stream=None) -> None:
+    arr, n = _planes(planes)
+    if stash_bytes is None:
+        stash_bytes = stash.numel() * stash.element_size()
+    _check(lib().qsa_rollback_gather(arr, n, _ptr(pages), _ptr(within), int(num_rows), _ptr(stash),
+                                     int(stash_bytes), _ptr(error_word), _stream(stream)), "qsa_rollback_gather")
+
+
+def qsa_rollback_restore(planes, pages, within, rejected, num_rows: int, stash, stash_bytes: Optional[int] = None,
+                         error_word=None, stream=None) -> None:
+    arr, n = _planes(planes)
+    if stash_bytes is None:
+        stash_bytes = stash.numel() * stash.element_size()
+    _check(lib().qsa_rollback_restore(arr, n, _ptr(pages), _ptr(within), _ptr(rejected), int(num_rows), _ptr(stash),
+                                      int(stash_bytes), _ptr(error_word), _stream(stream)), "qsa_rollback_restore")

@@ -86,6 +86,19 @@ class DeviceBatch:
                      self.v_scales.data_ptr(), self.index_keys.data_ptr(), self.k_global, self.v_global,
                      self.error_word.data_ptr() if error_word else None)
 
+    def rollback_planes(self):
+        """The cache's planes as rollback planes: k_codes, k_scales, v_codes, v_scales (a row
+        is one token slot across the KV heads) and index_keys (a row is one page)."""
+        from . import Plane
+        out = []
+        for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales):
+            NP, Hkv, P, nb = t.shape
+            out.append(Plane(t.data_ptr(), t.numel(), Hkv * P * nb, nb, P * nb, nb, Hkv, NP, P, 0))
+        NP, Hkv, d = self.index_keys.shape
+        out.append(Plane(self.index_keys.data_ptr(), self.index_keys.numel() * 2, Hkv * d * 2, 0, d * 2, d * 2, Hkv,
+                         NP, self.page_size, 0))
+        return out
+
     # output buffers ----------------------------------------------------------------
     def new_scores(self) -> torch.Tensor:
         return torch.empty((self.num_rows, self.max_pages), dtype=torch.float32, device=self.q.device)

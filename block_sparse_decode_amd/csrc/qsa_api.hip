@@ -386,3 +386,128 @@ qsa_status qsa_nvfp4_dequant_pages(const qsa_shape *sh, const uint8_t *codes, co
 }
 
 }  // extern "C"
+
+namespace {
+
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Validates the plane descriptors and fills the device descriptors with the stash offsets;
+// returns the stash size, or 0 (with ok = false) when anything is invalid.
+size_t plan_planes(const qsa_plane *planes, int32_t n, int32_t nrows, PlaneDesc *out, bool &ok)
+{
+    ok = false;
+    if (!planes || n < 1 || n > QSA_MAX_PLANES || nrows < 0) return 0;
+    unsigned __int128 off = 0;
+    for (int k = 0; k < n; ++k) {
+        const qsa_plane &p = planes[k];
+        if (!p.base || !aligned4(p.base) || p.plane_bytes <= 0 || p.page_stride < 0 || p.slot_stride < 0 ||
+            p.seg_stride < 0 || p.seg_bytes <= 0 || p.nseg < 1 || p.num_pages < 0 || p.num_slots < 1)
+            return 0;
+        if ((p.page_stride | p.slot_stride | p.seg_stride | (int64_t)p.seg_bytes) & 3) return 0;
+        if (p.num_pages > 0) {
+            // the last byte any (page, slot, segment) can address must lie inside the plane
+            const unsigned __int128 last = (unsigned __int128)(p.num_pages - 1) * (uint64_t)p.page_stride +
+                                           (unsigned __int128)(p.num_slots - 1) * (uint64_t)p.slot_stride +
+                                           (unsigned __int128)(p.nseg - 1) * (uint64_t)p.seg_stride +
+                                           (uint64_t)p.seg_bytes;
+            if (last > (unsigned __int128)p.plane_bytes) return 0;
+        }
+        const unsigned __int128 row = (unsigned __int128)p.nseg * (uint64_t)p.seg_bytes;
+        if (row / 4 > (1u << 24)) return 0;         // a row of at most 64 MiB
+        if (out) {
+            out[k].base = reinterpret_cast<char *>(p.base);
+            out[k].page_stride = p.page_stride;
+            out[k].slot_stride = p.slot_stride;
+            out[k].seg_stride = p.seg_stride;
+            out[k].num_pages = p.num_pages;
+            out[k].stash_off = (int64_t)off;
+            out[k].seg_words = p.seg_bytes / 4;
+            out[k].nseg = p.nseg;
+            out[k].num_slots = p.num_slots;
+            out[k].pad = 0;
+        }
+        off += (row * (uint64_t)nrows + 15) / 16 * 16;
+        if (off > ((unsigned __int128)1 << 62)) return 0;
+    }
+    ok = true;
+    return (size_t)off;
+}
+
+qsa_status rollback_call(const qsa_plane *planes, int32_t num_planes, const int32_t *pages, const int32_t *within,
+                         const int32_t *rejected, int32_t num_rows, const void *stash, size_t stash_bytes,
+                         uint32_t *error_word, void *stream, bool restore)
+{
+    RollbackParams prm;
+    bool ok = false;
+    const size_t need = plan_planes(planes, num_planes, num_rows, prm.planes, ok);
+    if (!ok) return QSA_ERR_INVALID_ARG;
+    if (error_word && !aligned4(error_word)) return QSA_ERR_INVALID_ARG;
+    if (num_rows == 0) return QSA_OK;
+    if (!pages || !within || !aligned4(pages) || !aligned4(within)) return QSA_ERR_INVALID_ARG;
+    if (restore && (!rejected || !aligned4(rejected))) return QSA_ERR_INVALID_ARG;
+    if (!stash || !aligned16(stash)) return QSA_ERR_INVALID_ARG;
+    if (stash_bytes < need) return QSA_ERR_WORKSPACE_TOO_SMALL;
+    prm.pages = pages;
+    prm.within = within;
+    prm.rejected = rejected;
+    prm.stash = reinterpret_cast<char *>(const_cast<void *>(stash));
+    prm.err = error_word;
+    prm.nrows = num_rows;
+    const hipError_t e = launch_rollback(prm, num_planes, restore, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qsa_rollback_stash_bytes(const qsa_plane *planes, int32_t num_planes, int32_t num_rows)
+{
+    bool ok = false;
+    const size_t n = plan_planes(planes, num_planes, num_rows, nullptr, ok);
+    return ok ? n : 0;
+}
+
+qsa_status qsa_rollback_gather(const qsa_plane *planes, int32_t num_planes, const int32_t *pages,
+                               const int32_t *within, int32_t num_rows, void *stash, size_t stash_bytes,
+                               uint32_t *error_word, void *stream)
+{
+    return rollback_call(planes, num_planes, pages, within, nullptr, num_rows, stash, stash_bytes, error_word,
+                         stream, false);
+}
+
+qsa_status qsa_rollback_restore(const qsa_plane *planes, int32_t num_planes, const int32_t *pages,
+                                const int32_t *within, const int32_t *rejected, int32_t num_rows,
+                                const void *stash, size_t stash_bytes, uint32_t *error_word, void *stream)
+{
+    return rollback_call(planes, num_planes, pages, within, rejected, num_rows, stash, stash_bytes, error_word,
+                         stream, true);
+}
+
+qsa_status qsa_step_slots(const qsa_shape *sh, const qsa_paged *pg, int32_t *pages, int32_t *within,
+                          void *stream)
+{
+    qsa_status st = check_shape(sh);
+    if (st != QSA_OK) return st;
+    if ((st = check_rows_ptrs(pg)) != QSA_OK) return st;
+    if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
+    if (!pg->page_table || !aligned16(pg->page_table) || !pages || !within || !aligned4(pages) ||
+        !aligned4(within))
+        return QSA_ERR_INVALID_ARG;
+    SlotParams prm;
+    prm.page_table = pg->page_table;
+    prm.seq_lens = pg->seq_lens;
+    prm.row_offsets = pg->row_offsets;
+    prm.pages = pages;
+    prm.within = within;
+    prm.err = pg->error_word;
+    prm.NP = sh->num_phys_pages;
+    prm.N = sh->num_rows;
+    prm.MP = sh->max_pages;
+    prm.P = sh->page_size;
+    prm.rmax = sh->max_rows_per_request;
+    const hipError_t e = launch_step_slots(prm, sh->num_requests, (hipStream_t)stream);
+    return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
+}
+
+}  // extern "C"

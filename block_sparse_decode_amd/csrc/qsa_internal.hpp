@@ -90,6 +90,42 @@ hipError_t launch_select_sparse_decode(const DecodeParams &prm, int D, hipStream
 hipError_t launch_dequant_pages(const DequantParams &prm, int D, hipStream_t stream);
 hipError_t launch_kv_store(const StoreParams &prm, int D, int B, hipStream_t stream);
 
+// ---- rollback ---------------------------------------------------------------------------
+struct PlaneDesc {
+    char *base;
+    int64_t page_stride, slot_stride, seg_stride;
+    int64_t num_pages;
+    int64_t stash_off;          // byte offset of this plane's rows in the stash
+    int32_t seg_words;          // seg_bytes / 4
+    int32_t nseg;
+    int32_t num_slots;
+    int32_t pad;
+};
+
+struct RollbackParams {
+    PlaneDesc planes[QSA_MAX_PLANES];
+    const int32_t *pages;
+    const int32_t *within;
+    const int32_t *rejected;    // restore only
+    char *stash;
+    uint32_t *err;
+    int32_t nrows;
+};
+
+struct SlotParams {
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    const int32_t *row_offsets;
+    int32_t *pages;
+    int32_t *within;
+    uint32_t *err;
+    int64_t NP;
+    int32_t N, MP, P, rmax;
+};
+
+hipError_t launch_rollback(const RollbackParams &prm, int num_planes, bool restore, hipStream_t stream);
+hipError_t launch_step_slots(const SlotParams &prm, int B, hipStream_t stream);
+
 // number of waves per decode workgroup
 constexpr int kDecodeWaves = 8;
 

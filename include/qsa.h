@@ -53,6 +53,7 @@ typedef enum qsa_status {
 #define QSA_DEVERR_ROWS       0x4u   /* row_offsets not non-decreasing, or a request with > max rows */
 #define QSA_DEVERR_Q_RANGE    0x8u   /* a q element beyond the f16 range (|q| > 65504) */
 #define QSA_DEVERR_SELECTED   0x10u  /* a selected entry outside [-1, MP): ignored */
+#define QSA_DEVERR_SLOT       0x20u  /* a rollback row's slot outside [0, num_slots): skipped */
 
 /* Sizes of one call. Host memory, read during the call only. */
 typedef struct qsa_shape {
@@ -208,6 +209,80 @@ qsa_status qsa_select_sparse_decode(const qsa_shape *shape, const qsa_paged *pag
  */
 qsa_status qsa_kv_store(const qsa_shape *shape, const qsa_paged *paged,
                         const uint16_t *new_k, const uint16_t *new_v, void *stream);
+
+/*
+ * Index-plane rollback (PR #20937, Description > What changes > Rollback and PLE: a batched
+ * rollback of the QSA index planes; its rollback gather / restore operation). Before a
+ * verify step stores its draft rows, qsa_rollback_gather saves the plane rows those rows
+ * will overwrite; after acceptance, qsa_rollback_restore writes the saved bytes back for the
+ * rejected rows. Kept rows, and every other byte, stay as the step left them.
+ *
+ * A plane is caller-owned device memory. Row r of a plane (for step row r) is the nseg
+ * segments of seg_bytes bytes at
+ *     base + pages[r] * page_stride + within[r] * slot_stride + s * seg_stride,  s < nseg
+ * (slot_stride 0: one row per page, such as the index keys). Every row that pages in
+ * [0, num_pages) and slots in [0, num_slots) can address must lie in [base, base +
+ * plane_bytes), base and all strides and seg_bytes must be multiples of 4; else the call
+ * returns QSA_ERR_INVALID_ARG. For the paged cache of this library the planes are
+ * k_codes / k_scales / v_codes / v_scales (page_stride Hkv*P*b, slot_stride b, seg_stride
+ * P*b, seg_bytes b, nseg Hkv, with b the bytes per token and head) and index_keys
+ * (page_stride Hkv*d*2, slot_stride 0, seg_stride d*2, seg_bytes d*2, nseg Hkv).
+ */
+typedef struct {
+    void *base;                /* device */
+    int64_t plane_bytes;
+    int64_t page_stride;
+    int64_t slot_stride;
+    int64_t seg_stride;
+    int32_t seg_bytes;
+    int32_t nseg;
+    int64_t num_pages;
+    int32_t num_slots;
+    int32_t reserved;          /* 0 */
+} qsa_plane;
+
+#define QSA_MAX_PLANES 16
+
+/*
+ * Stash size for num_rows rows of these planes: plane k's rows are stored contiguously,
+ * row r at offset_k + r * row_bytes_k (row_bytes = nseg * seg_bytes), with offset_k the sum
+ * over earlier planes of num_rows * row_bytes rounded up to 16 bytes. 0 for invalid input.
+ */
+size_t qsa_rollback_stash_bytes(const qsa_plane *planes, int32_t num_planes, int32_t num_rows);
+
+/*
+ * The (physical page, slot) that each row of a verify step occupies in the paged cache,
+ * the placement qsa_kv_store uses: row j of request b (R_b rows, length L) is the token at
+ * position L - R_b + j. pages[r] = page_table[b][pos / P] (or -1 when pos < 0, pos / P >=
+ * max_pages, or the entry is invalid; an entry outside [-1, NP) sets QSA_DEVERR_PAGE_ID),
+ * within[r] = pos % P (0 when the page is -1). pages, within: int32 [N] (device, written).
+ */
+qsa_status qsa_step_slots(const qsa_shape *shape, const qsa_paged *paged, int32_t *pages,
+                          int32_t *within, void *stream);
+
+/*
+ * stash[plane k][row r] = row r of plane k, for every row whose page is in [0, num_pages)
+ * and slot in [0, num_slots). A row with page -1 is skipped; any other page or slot out of
+ * range is skipped and sets QSA_DEVERR_PAGE_ID / QSA_DEVERR_SLOT in error_word (optional).
+ * Skipped rows leave their stash bytes unchanged.
+ *   pages, within  int32 [num_rows] (device)
+ *   stash          device, at least qsa_rollback_stash_bytes bytes, 16-byte aligned
+ */
+qsa_status qsa_rollback_gather(const qsa_plane *planes, int32_t num_planes, const int32_t *pages,
+                               const int32_t *within, int32_t num_rows, void *stash,
+                               size_t stash_bytes, uint32_t *error_word, void *stream);
+
+/*
+ * Row r of plane k = stash[k][r] for every row with rejected[r] != 0 (rows skipped as in
+ * qsa_rollback_gather). rejected: int32 [num_rows] (device). Rows of distinct (page, slot)
+ * per plane are written independently; rows that address the same bytes (two step rows in
+ * one page of a per-page plane) must carry the same stashed bytes, which a gather of the
+ * same rows guarantees.
+ */
+qsa_status qsa_rollback_restore(const qsa_plane *planes, int32_t num_planes, const int32_t *pages,
+                                const int32_t *within, const int32_t *rejected, int32_t num_rows,
+                                const void *stash, size_t stash_bytes, uint32_t *error_word,
+                                void *stream);
 
 /*
  * Parity hook: NVFP4 dequantisation of whole pages through the same device decode that

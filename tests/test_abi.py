@@ -174,6 +174,81 @@ def test_kv_store_validation():
                 None) == 0
 
 
+def test_plane_struct_layout(tmp_path):
+    prog = tmp_path / "plane.c"
+    prog.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "qsa.h"
+int main(void) {
+  printf("%zu %zu %zu %zu %zu %zu\n", sizeof(qsa_plane), offsetof(qsa_plane, plane_bytes),
+         offsetof(qsa_plane, seg_bytes), offsetof(qsa_plane, nseg), offsetof(qsa_plane, num_pages),
+         offsetof(qsa_plane, num_slots));
+  return 0;
+}
+''')
+    exe = tmp_path / "plane"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
+    got = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()))
+    P = q.Plane
+    assert got == [ctypes.sizeof(P), P.plane_bytes.offset, P.seg_bytes.offset, P.nseg.offset, P.num_pages.offset,
+                   P.num_slots.offset]
+
+
+def _plane(**kw):
+    base = dict(base=FAKE, plane_bytes=4 * 3 * 64 * 64, page_stride=3 * 64 * 64, slot_stride=64, seg_stride=64 * 64,
+                seg_bytes=64, nseg=3, num_pages=4, num_slots=64, reserved=0)
+    base.update(kw)
+    return q.Plane(**base)
+
+
+def test_rollback_stash_bytes():
+    # plane k's rows at a 16-byte aligned offset after the earlier planes' rows
+    a, b = _plane(), _plane(seg_bytes=4, slot_stride=4, seg_stride=4 * 64, page_stride=3 * 64 * 4,
+                            plane_bytes=4 * 3 * 64 * 4)
+    assert q.qsa_rollback_stash_bytes([a], 5) == 5 * 192
+    assert q.qsa_rollback_stash_bytes([b, a], 5) == 64 + 5 * 192          # 5 * 12 = 60 -> 64
+    assert q.qsa_rollback_stash_bytes([a, b], 0) == 0
+    # invalid descriptors give 0
+    for bad in (dict(base=None), dict(base=FAKE + 2), dict(seg_bytes=6), dict(seg_bytes=0), dict(nseg=0),
+                dict(num_slots=0), dict(page_stride=-64), dict(slot_stride=66), dict(plane_bytes=4 * 3 * 64 * 64 - 1),
+                dict(num_pages=-1)):
+        assert q.qsa_rollback_stash_bytes([_plane(**bad)], 5) == 0, bad
+    assert q.qsa_rollback_stash_bytes([a] * 17, 5) == 0
+    assert q.qsa_rollback_stash_bytes([a], -1) == 0
+    assert q.qsa_rollback_stash_bytes([], 5) == 0
+
+
+def test_rollback_validation():
+    arr = (q.Plane * 2)(_plane(), _plane())
+    g = lambda planes, n, pages, within, rows, stash, sb: _raw("qsa_rollback_gather", planes, n, pages, within, rows,
+                                                               stash, sb, None, None)
+    r = lambda planes, n, pages, within, rej, rows, stash, sb: _raw("qsa_rollback_restore", planes, n, pages, within,
+                                                                    rej, rows, stash, sb, None, None)
+    need = q.qsa_rollback_stash_bytes(list(arr), 8)
+    assert g(arr, 2, None, None, 0, None, 0) == 0                       # no rows: no-op
+    assert g(arr, 2, None, FAKE, 8, FAKE, need) == 1
+    assert g(arr, 2, FAKE, FAKE + 2, 8, FAKE, need) == 1
+    assert g(arr, 2, FAKE, FAKE, 8, None, need) == 1
+    assert g(arr, 2, FAKE, FAKE, 8, FAKE + 8, need) == 1                # stash 16-byte aligned
+    assert g(arr, 2, FAKE, FAKE, 8, FAKE, need - 1) == 3
+    assert g(arr, 0, FAKE, FAKE, 8, FAKE, need) == 1
+    assert g(None, 2, FAKE, FAKE, 8, FAKE, need) == 1
+    bad = (q.Plane * 1)(_plane(seg_bytes=6))
+    assert g(bad, 1, FAKE, FAKE, 8, FAKE, need) == 1
+    assert r(arr, 2, FAKE, FAKE, None, 8, FAKE, need) == 1              # rejected flags required
+    assert r(arr, 2, FAKE, FAKE, FAKE, 8, FAKE, need - 1) == 3
+    assert r(arr, 2, None, None, None, 0, None, 0) == 0
+    assert _raw("qsa_rollback_gather", arr, 2, FAKE, FAKE, 8, FAKE, need, FAKE + 2, None) == 1   # error word
+    # step slots: the shape checks apply; outputs required
+    sh, pg = _shape(), _paged()
+    assert _raw("qsa_step_slots", ctypes.byref(_shape(head_dim=96)), ctypes.byref(pg), FAKE, FAKE, None) == 2
+    assert _raw("qsa_step_slots", ctypes.byref(sh), ctypes.byref(pg), None, FAKE, None) == 1
+    assert _raw("qsa_step_slots", ctypes.byref(sh), ctypes.byref(_paged(page_table=None)), FAKE, FAKE, None) == 1
+    assert _raw("qsa_step_slots", ctypes.byref(_shape(num_requests=0, num_rows=0)), ctypes.byref(pg), None, None,
+                None) == 0
+
+
 def test_workspace_sizing():
     sh = _shape()
     assert q.qsa_workspace_bytes(sh, 1) == 0
