@@ -307,10 +307,44 @@ def main():
         if status != 0:
             raise q.QsaError(status, "qsa_kv_store")
     store_us = stage_us(store)
+
+    # (4) the rollback around a verify step: gather the plane rows the step's rows overwrite,
+    # and restore half of them (the rejected drafts)
+    ctx = {}
+    for st in steps:
+        n = w.N
+        pages = torch.empty(n, dtype=torch.int32, device=dev)
+        within = torch.empty(n, dtype=torch.int32, device=dev)
+        q.qsa_step_slots(st.shape_, st.paged_, pages, within, stream)
+        planes = st.b.rollback_planes()
+        arr = (q.Plane * len(planes))(*planes)
+        sb = q.qsa_rollback_stash_bytes(planes, n)
+        stash = torch.zeros(sb, dtype=torch.uint8, device=dev)
+        rej = torch.from_numpy((np.arange(n) % 2).astype(np.int32)).to(dev)
+        ctx[id(st)] = (arr, len(planes), pages, within, rej, stash, sb)
+
+    def gather(st):
+        arr, npl, pages, within, rej, stash, sb = ctx[id(st)]
+        status = L.qsa_rollback_gather(arr, npl, pages.data_ptr(), within.data_ptr(), w.N, stash.data_ptr(), sb,
+                                       None, stream.cuda_stream)
+        if status != 0:
+            raise q.QsaError(status, "qsa_rollback_gather")
+
+    def restore(st):
+        arr, npl, pages, within, rej, stash, sb = ctx[id(st)]
+        status = L.qsa_rollback_restore(arr, npl, pages.data_ptr(), within.data_ptr(), rej.data_ptr(), w.N,
+                                        stash.data_ptr(), sb, None, stream.cuda_stream)
+        if status != 0:
+            raise q.QsaError(status, "qsa_rollback_restore")
+    gather_us = stage_us(gather)
+    restore_us = stage_us(restore)
+    row_bytes = sum(pl.nseg * pl.seg_bytes for pl in steps[0].b.rollback_planes())
     err = int(base.error_word[0].item())
 
     ab = algorithmic_bytes(w, sel)
     ab["kv_store"] = store_bytes(w)
+    ab["rollback_gather"] = 2 * w.N * row_bytes                 # read the rows, write the stash
+    ab["rollback_restore"] = 2 * (w.N // 2) * row_bytes         # half the rows rejected
     us_step = wall / K * 1e6
     achieved = ab["select_attention"] / (fus_us * 1e-6) / 1e9
     step_gbs = ab["step"] / (us_step * 1e-6) / 1e9
@@ -339,6 +373,7 @@ def main():
                    "separate_select_topk_us": round(sel_us, 2), "separate_sparse_decode_us": round(dec_us, 2),
                    "kv_store_us": round(store_us, 2),
                    "kv_store_gbs": round(ab["kv_store"] / (store_us * 1e-6) / 1e9, 1),
+                   "rollback_gather_us": round(gather_us, 2), "rollback_restore_us": round(restore_us, 2),
                    "timing": "mean of back-to-back launches between one HIP event pair on the launch stream"},
         "bytes": ab,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
