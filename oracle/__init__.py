@@ -16,7 +16,9 @@ Parity status (see tests/test_oracle_*.py):
   index scores         pinned: integer-exact cases, fp64 error bound, per-head brute force
   selection            pinned: brute force over all tie patterns, invariants
   attention            pinned: brute-force dense softmax, torch SDPA (fp64) on full windows,
-                       single-token and equal-key closed forms
+                       single-token and equal-key closed forms; the FP8 format against a
+                       dense softmax over table-decoded bytes; the gate against scipy's
+                       expit, gate 0 (exact half) and a saturating gate (unchanged)
   KV store             pinned: brute-force nearest-code search over every E2M1 / E4M3 code,
                        exactly representable blocks, closed-form index keys
   rollback (rollback.py, numpy)
@@ -79,9 +81,11 @@ def _declare(L):
     L.oracle_index_scores.argtypes = [_I, _P, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _F, _P, _P, _P]
     L.oracle_select.argtypes = [_I, _P, _P, _I, _I, _I, _I, _P, _P]
     L.oracle_attention.argtypes = [_I, _P, _P, _P, _I, _I64, _I, _I, _I, _I, _F, _D, _D,
-                                   _P, _P, _P, _P, _P, _P, _I, _P, _P]
+                                   _P, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P]
     L.oracle_attention_one.argtypes = [_I, _P, _P, _P, _I, _I64, _I, _I, _I, _I, _F, _D, _D,
-                                       _P, _P, _P, _P, _P, _P, _I, _I, _I, _P, _P]
+                                       _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _P, _P]
+    L.oracle_fp8_elem.argtypes = [_P, _D, _I, _I, _I, _I64, _I, _I, _I]
+    L.oracle_fp8_elem.restype = _D
     L.oracle_e4m3_encode.argtypes = [_F]
     L.oracle_e4m3_encode.restype = ctypes.c_uint8
     L.oracle_e2m1_encode.argtypes = [_F]
@@ -172,41 +176,46 @@ def select_w(w, scores):
     return select(w.seq_lens, w.row_offsets, c.page_size, w.MP, c.topk, c.window, scores)
 
 
-def _attn_args(w, selected, sm_scale):
+KV_FORMATS = {"nvfp4": 0, "fp8": 1}
+
+
+def _attn_args(w, selected, sm_scale, gate):
     c = w.cfg
     arrs = dict(
         sl=_c(w.seq_lens, np.int32), ro=_c(w.row_offsets, np.int32), pt=_c(w.page_table, np.int32),
         q=_c(w.q, np.uint16), kc=_c(w.k_codes, np.uint8), ks=_c(w.k_scales, np.uint8),
         vc=_c(w.v_codes, np.uint8), vs=_c(w.v_scales, np.uint8), sel=_c(selected, np.int32))
+    arrs["gate"] = _c(gate, np.uint16) if gate is not None else (None, None)
     s = np.float32(w.sm_scale if sm_scale is None else sm_scale)
-    return c, arrs, s
+    return c, arrs, s, KV_FORMATS[getattr(c, "kv_format", "nvfp4")]
 
 
-def attention(w, selected, sm_scale=None):
-    """fp64 (out [N][Hq][d], lse [N][Hq]) for workload `w` and selection rows."""
-    c, a, s = _attn_args(w, selected, sm_scale)
+def attention(w, selected, sm_scale=None, gate=None):
+    """fp64 (out [N][Hq][d], lse [N][Hq]) for workload `w` and selection rows; `gate`
+    (bf16 bits [N][Hq][d], optional) multiplies out by its sigmoid."""
+    c, a, s, fmt = _attn_args(w, selected, sm_scale, gate)
     N, Hq, d = w.q.shape
     sel = a["sel"][0]
     out = np.empty((N, Hq, d), np.float64)
     lse = np.empty((N, Hq), np.float64)
     lib().oracle_attention(w.B, a["sl"][1], a["ro"][1], a["pt"][1], w.MP, w.NP, c.page_size,
                            Hq, c.kv_heads, d, s, c.k_global, c.v_global, a["q"][1], a["kc"][1],
-                           a["ks"][1], a["vc"][1], a["vs"][1], a["sel"][1], sel.shape[1],
-                           out.ctypes.data_as(_P), lse.ctypes.data_as(_P))
+                           a["ks"][1], a["vc"][1], a["vs"][1], fmt, a["sel"][1], sel.shape[1],
+                           a["gate"][1], out.ctypes.data_as(_P), lse.ctypes.data_as(_P))
     return out, lse
 
 
-def attention_one(w, selected, row, head, sm_scale=None):
+def attention_one(w, selected, row, head, sm_scale=None, gate=None):
     """fp64 (out [d], lse) for one (row, q head)."""
-    c, a, s = _attn_args(w, selected, sm_scale)
+    c, a, s, fmt = _attn_args(w, selected, sm_scale, gate)
     N, Hq, d = w.q.shape
     sel = a["sel"][0]
     out = np.empty(d, np.float64)
     lse = np.empty(1, np.float64)
     lib().oracle_attention_one(w.B, a["sl"][1], a["ro"][1], a["pt"][1], w.MP, w.NP, c.page_size,
                                Hq, c.kv_heads, d, s, c.k_global, c.v_global, a["q"][1],
-                               a["kc"][1], a["ks"][1], a["vc"][1], a["vs"][1], a["sel"][1],
-                               sel.shape[1], int(row), int(head), out.ctypes.data_as(_P),
+                               a["kc"][1], a["ks"][1], a["vc"][1], a["vs"][1], fmt, a["sel"][1],
+                               sel.shape[1], a["gate"][1], int(row), int(head), out.ctypes.data_as(_P),
                                lse.ctypes.data_as(_P))
     return out, float(lse[0])
 

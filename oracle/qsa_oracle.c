@@ -87,6 +87,22 @@ double oracle_dequant_elem(const uint8_t *codes, const uint8_t *scales, double g
     return oracle_e2m1(c) * oracle_e4m3(sb) * global;
 }
 
+/* One element of an FP8 page [PR20937, the FP8 KV cache of the tested configurations: unit
+   scales]: codes [NP][Hkv][P][d] hold one OCP E4M3FN byte per element, x = e4m3(byte) * global. */
+double oracle_fp8_elem(const uint8_t *codes, double global, int Hkv, int P, int d, int64_t page, int h, int t, int i)
+{
+    int64_t tok = ((page * Hkv + h) * P + t);
+    return oracle_e4m3(codes[tok * d + i]) * global;
+}
+
+/* The element of either cache format: kv_format 0 = NVFP4, 1 = FP8 (scales unused). */
+static double kv_elem(int kv_format, const uint8_t *codes, const uint8_t *scales, double global,
+                      int Hkv, int P, int d, int64_t page, int h, int t, int i)
+{
+    return kv_format == 1 ? oracle_fp8_elem(codes, global, Hkv, P, d, page, h, t, i)
+                          : oracle_dequant_elem(codes, scales, global, Hkv, P, d, page, h, t, i);
+}
+
 /* Dequantise the listed physical pages: out[j][h][t][i] for j < n (fp64). */
 void oracle_dequant_pages(const uint8_t *codes, const uint8_t *scales, double global,
                           int Hkv, int P, int d, const int32_t *pages, int n, double *out)
@@ -256,13 +272,16 @@ void oracle_select(int B, const int32_t *seq_lens, const int32_t *row_offsets, i
        logit_t = sm_scale * sum_i q[h][i] * K_t[i]        (K, V dequantised, fp64)
        out[h]  = sum_t exp(logit_t - m) V_t / sum_t exp(logit_t - m),  m = max logit
        lse[h]  = m + ln(sum_t exp(logit_t - m))
-   An empty T gives out = 0 and lse = -inf. */
+   An empty T gives out = 0 and lse = -inf. With a gate [PR20937, What changes > MTP >
+   Verify: the gated epilogue], out[h][i] is multiplied by sigmoid(gate[row][h][i]) =
+   1 / (1 + exp(-g)), g the bf16 gate value; lse is not gated. kv_format selects the cache
+   format of K and V (0 NVFP4, 1 FP8). */
 void oracle_attention(int B, const int32_t *seq_lens, const int32_t *row_offsets,
                       const int32_t *page_table, int MP, int64_t NP, int P,
                       int Hq, int Hkv, int d, float sm_scale, double k_global, double v_global,
                       const uint16_t *q, const uint8_t *k_codes, const uint8_t *k_scales,
-                      const uint8_t *v_codes, const uint8_t *v_scales,
-                      const int32_t *selected, int sel_width, double *out, double *lse)
+                      const uint8_t *v_codes, const uint8_t *v_scales, int kv_format,
+                      const int32_t *selected, int sel_width, const uint16_t *gate, double *out, double *lse)
 {
     int N = row_offsets[B];
     int32_t *rq = malloc(sizeof(int32_t) * (N > 0 ? N : 1));
@@ -308,7 +327,7 @@ void oracle_attention(int B, const int32_t *seq_lens, const int32_t *row_offsets
                 double dot = 0.0;
                 for (int i = 0; i < d; ++i)
                     dot += oracle_bf16(qv[i]) *
-                           oracle_dequant_elem(k_codes, k_scales, k_global, Hkv, P, d, tp[t], g, tt[t], i);
+                           kv_elem(kv_format, k_codes, k_scales, k_global, Hkv, P, d, tp[t], g, tt[t], i);
                 logit[t] = (double)sm_scale * dot;
                 if (logit[t] > m) m = logit[t];
             }
@@ -317,9 +336,13 @@ void oracle_attention(int B, const int32_t *seq_lens, const int32_t *row_offsets
                 double w = exp(logit[t] - m);
                 l += w;
                 for (int i = 0; i < d; ++i)
-                    o[i] += w * oracle_dequant_elem(v_codes, v_scales, v_global, Hkv, P, d, tp[t], g, tt[t], i);
+                    o[i] += w * kv_elem(kv_format, v_codes, v_scales, v_global, Hkv, P, d, tp[t], g, tt[t], i);
             }
             for (int i = 0; i < d; ++i) o[i] /= l;
+            if (gate) {
+                const uint16_t *gv = gate + ((int64_t)r * Hq + h) * d;
+                for (int i = 0; i < d; ++i) o[i] *= 1.0 / (1.0 + exp(-oracle_bf16(gv[i])));
+            }
             lse[(int64_t)r * Hq + h] = m + log(l);
         }
     }
@@ -338,8 +361,8 @@ void oracle_attention_one(int B, const int32_t *seq_lens, const int32_t *row_off
                           const int32_t *page_table, int MP, int64_t NP, int P,
                           int Hq, int Hkv, int d, float sm_scale, double k_global, double v_global,
                           const uint16_t *q, const uint8_t *k_codes, const uint8_t *k_scales,
-                          const uint8_t *v_codes, const uint8_t *v_scales,
-                          const int32_t *selected, int sel_width, int row, int head,
+                          const uint8_t *v_codes, const uint8_t *v_scales, int kv_format,
+                          const int32_t *selected, int sel_width, const uint16_t *gate, int row, int head,
                           double *out_d, double *lse_1)
 {
     /* Run the full definition on a one-row, one-head view of the batch. */
@@ -361,10 +384,14 @@ void oracle_attention_one(int B, const int32_t *seq_lens, const int32_t *row_off
     double *o = malloc(sizeof(double) * (size_t)R * Hkv * d);
     double *ls = malloc(sizeof(double) * (size_t)R * Hkv);
     oracle_attention(1, seq_lens + b, ro, page_table + (int64_t)b * MP, MP, NP, P, Hkv, Hkv, d,
-                     sm_scale, k_global, v_global, qv, k_codes, k_scales, v_codes, v_scales,
-                     sel, sel_width, o, ls);
+                     sm_scale, k_global, v_global, qv, k_codes, k_scales, v_codes, v_scales, kv_format,
+                     sel, sel_width, NULL, o, ls);
     memcpy(out_d, o + ((size_t)jrow * Hkv + g) * d, sizeof(double) * d);
     *lse_1 = ls[(size_t)jrow * Hkv + g];
+    if (gate) {
+        const uint16_t *gv = gate + ((int64_t)row * Hq + head) * d;
+        for (int i = 0; i < d; ++i) out_d[i] *= 1.0 / (1.0 + exp(-oracle_bf16(gv[i])));
+    }
     free(sel);
     free(qv);
     free(o);

@@ -43,7 +43,7 @@ import numpy as np
 
 __all__ = [
     "Config", "Workload", "CONFIGS", "generate", "bf16_bits_from_f32",
-    "f32_from_bf16_bits", "encode_nvfp4", "encode_e4m3", "E4M3_POS_VALUES",
+    "f32_from_bf16_bits", "encode_nvfp4", "encode_e4m3", "encode_fp8", "E4M3_POS_VALUES",
 ]
 
 # --------------------------------------------------------------------------
@@ -121,6 +121,15 @@ def encode_nvfp4(x: np.ndarray, global_scale: float = 1.0) -> Tuple[np.ndarray, 
     return np.ascontiguousarray(packed), np.ascontiguousarray(s_code)
 
 
+def encode_fp8(x: np.ndarray, global_scale: float = 1.0) -> np.ndarray:
+    """Quantise float32 `x` to signed E4M3FN bytes with a unit block scale: the code nearest
+    to x / global (RNE, saturating at +-448; +0 for values that round to zero)."""
+    y = np.asarray(x, dtype=np.float64) / float(global_scale)
+    mag = encode_e4m3(np.abs(y))
+    sign = (np.signbit(y) & (mag != 0)).astype(np.uint8) << 7
+    return np.ascontiguousarray(mag | sign)
+
+
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     """Round finite float32 values to bf16 (RNE) and return the 16-bit patterns."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -172,6 +181,7 @@ class Config:
     k_global: float = 1.0
     v_global: float = 1.0
     max_pages: Optional[int] = None  # page-table stride; default = max pages per request
+    kv_format: str = "nvfp4"     # "nvfp4": e2m1 codes + e4m3 block scales; "fp8": e4m3 bytes, unit scales
 
     def with_(self, **kw) -> "Config":
         return dataclasses.replace(self, **kw)
@@ -258,7 +268,10 @@ def _fill_chunk(args):
             x.reshape(-1)[pos] = sgn * np.float32(cfg.outlier_value)
         x *= live[:, None, :, None]                                          # tokens past L_b are zero
         gs = cfg.k_global if which == "k" else cfg.v_global
-        codes, scales = encode_nvfp4(x, gs)
+        if cfg.kv_format == "fp8":
+            codes, scales = encode_fp8(x, gs), np.zeros(x.shape[:-1] + (0,), np.uint8)
+        else:
+            codes, scales = encode_nvfp4(x, gs)
         if which == "k":
             k_codes[c0:c1], k_scales[c0:c1] = codes, scales
             cnt_t = np.maximum(valid_tokens[c0:c1], 1).astype(np.float64)
@@ -318,10 +331,12 @@ def generate(cfg, threads: Optional[int] = None) -> Workload:
     q = bf16_bits_from_f32(rng.standard_normal((N, Hq, d), dtype=np.float32))
 
     # K / V pages in physical-page order, one child seed per chunk
-    k_codes = np.empty((NP, Hkv, P, d // 2), np.uint8)
-    v_codes = np.empty((NP, Hkv, P, d // 2), np.uint8)
-    k_scales = np.empty((NP, Hkv, P, d // 16), np.uint8)
-    v_scales = np.empty((NP, Hkv, P, d // 16), np.uint8)
+    assert cfg.kv_format in ("nvfp4", "fp8")
+    fp8 = cfg.kv_format == "fp8"
+    k_codes = np.empty((NP, Hkv, P, d if fp8 else d // 2), np.uint8)
+    v_codes = np.empty((NP, Hkv, P, d if fp8 else d // 2), np.uint8)
+    k_scales = np.empty((NP, Hkv, P, 0 if fp8 else d // 16), np.uint8)
+    v_scales = np.empty((NP, Hkv, P, 0 if fp8 else d // 16), np.uint8)
     index_keys = np.empty((NP, Hkv, d), np.uint16)
     valid_tokens = np.minimum(P, seq[owner_req].astype(np.int64) - owner_lp * P)  # per physical page
     starts = list(range(0, NP, CHUNK_PAGES))

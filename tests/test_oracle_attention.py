@@ -170,3 +170,92 @@ def test_attention_one_matches_full():
         for h in (0, w.cfg.q_heads - 1):
             o1, l1 = oracle.attention_one(w, sel, r, h)
             assert np.array_equal(o1, out[r, h]) and l1 == lse[r, h]
+
+
+# ---- FP8 KV cache (unit scales) and the gated epilogue ---------------------------------
+
+_E4M3_TABLE = np.array([oracle.e4m3(b) for b in range(256)])
+
+
+def _dense_fp8(w, selected):
+    """As _dense_reference, with K and V decoded as one E4M3FN byte per element."""
+    c = w.cfg
+    K = _E4M3_TABLE[w.k_codes] * c.k_global
+    V = _E4M3_TABLE[w.v_codes] * c.v_global
+    Hq, Hkv, P = c.q_heads, c.kv_heads, c.page_size
+    G = Hq // Hkv
+    q = synth.f32_from_bf16_bits(w.q).astype(np.float64)
+    out = np.zeros((w.N, Hq, c.head_dim))
+    lse = np.full((w.N, Hq), -np.inf)
+    for b in range(w.B):
+        r0, r1 = w.row_offsets[b], w.row_offsets[b + 1]
+        for j in range(r1 - r0):
+            r = r0 + j
+            L = max(0, int(w.seq_lens[b]) - (r1 - r0 - 1 - j))
+            toks = [(w.page_table[b, p], t) for p in sorted(set(int(x) for x in selected[r] if 0 <= x < w.MP))
+                    if 0 <= w.page_table[b, p] < w.NP for t in range(P) if p * P + t < L]
+            for h in range(Hq if toks else 0):
+                Kt = np.stack([K[ph, h // G, t] for ph, t in toks])
+                Vt = np.stack([V[ph, h // G, t] for ph, t in toks])
+                logits = w.sm_scale * (Kt @ q[r, h])
+                lse[r, h] = scipy.special.logsumexp(logits)
+                out[r, h] = np.exp(logits - lse[r, h]) @ Vt
+    return out, lse
+
+
+@pytest.mark.parametrize("kw", [dict(kv_format="fp8"), dict(kv_format="fp8", invalid_frac=0.2, seed=14, v_global=0.5),
+                                dict(kv_format="fp8", rows=4, context=(40, 130), seed=15)])
+def test_fp8_attention_matches_dense_bruteforce(kw):
+    w = _small(**kw)
+    assert w.k_codes.shape[-1] == w.cfg.head_dim and w.k_scales.shape[-1] == 0
+    sel = oracle.select_w(w, oracle.index_scores(w))
+    out, lse = oracle.attention(w, sel)
+    ref_out, ref_lse = _dense_fp8(w, sel)
+    assert np.allclose(out, ref_out, rtol=1e-12, atol=1e-12)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse)) and np.allclose(lse[fin], ref_lse[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_element_indexing():
+    """oracle_fp8_elem reads byte [page][h][t][i] of the [NP][Hkv][P][d] plane."""
+    w = _small(kv_format="fp8", seed=16)
+    c = w.cfg
+    rng = np.random.default_rng(0)
+    codes = np.ascontiguousarray(w.k_codes)
+    for _ in range(200):
+        pg, h, t, i = (int(rng.integers(n)) for n in codes.shape)
+        got = oracle.lib().oracle_fp8_elem(codes.ctypes.data_as(oracle._P), 2.0, c.kv_heads, c.page_size,
+                                           c.head_dim, pg, h, t, i)
+        assert got == 2.0 * _E4M3_TABLE[codes[pg, h, t, i]]
+
+
+def test_fp8_encoder_is_nearest():
+    """The generator's FP8 bytes decode to the nearest E4M3FN value (the recipe's stated rounding)."""
+    x = np.random.default_rng(1).standard_normal(20000).astype(np.float32) * 3
+    codes = synth.encode_fp8(x)
+    dec = _E4M3_TABLE[codes]
+    grid = np.concatenate([-synth.E4M3_POS_VALUES[::-1], synth.E4M3_POS_VALUES])
+    best = np.abs(grid[None, :] - x[:, None].astype(np.float64)).min(axis=1)
+    assert np.all(np.abs(dec - x) == best)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_gate_multiplies_by_sigmoid(fmt):
+    w = _small(kv_format=fmt, rows=4, context=(40, 130), seed=17)
+    sel = oracle.select_w(w, oracle.index_scores(w))
+    out, lse = oracle.attention(w, sel)
+    g = synth.bf16_bits_from_f32(np.random.default_rng(2).standard_normal(w.q.shape).astype(np.float32) * 3)
+    gout, glse = oracle.attention(w, sel, gate=g)
+    sig = scipy.special.expit(synth.f32_from_bf16_bits(g).astype(np.float64))
+    assert np.allclose(gout, out * sig, rtol=1e-14, atol=0)
+    assert np.array_equal(np.isfinite(glse), np.isfinite(lse))
+    assert np.array_equal(glse[np.isfinite(lse)], lse[np.isfinite(lse)])
+    # gate 0 halves the output exactly; a large gate leaves it unchanged
+    half, _ = oracle.attention(w, sel, gate=np.zeros_like(g))
+    assert np.array_equal(half, out * 0.5)
+    big = synth.bf16_bits_from_f32(np.full(w.q.shape, 64.0, np.float32))
+    same, _ = oracle.attention(w, sel, gate=big)
+    assert np.array_equal(same, out)
+    for r in range(w.N):
+        o1, _ = oracle.attention_one(w, sel, r, 1, gate=g)
+        assert np.array_equal(o1, gout[r, 1])
