@@ -179,9 +179,10 @@ def store_bytes(w):
 def fused_kernel_name(w):
     """Name rocprofv3 gives the fused selection + attention kernel for this workload."""
     c = w.cfg
+    fmt = 1 if getattr(c, "kv_format", "nvfp4") == "fp8" else 0
     if w.MP > 1024:
-        return f"sparse_decode_kernel<{c.head_dim}, 0>"
-    return f"sparse_decode_kernel<{c.head_dim}, {8 if w.MP <= 512 else 16}>"
+        return f"sparse_decode_kernel<{c.head_dim}, 0, {fmt}>"
+    return f"sparse_decode_kernel<{c.head_dim}, {8 if w.MP <= 512 else 16}, {fmt}>"
 
 
 def cpu_baseline(w, max_rows):

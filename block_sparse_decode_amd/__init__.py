@@ -33,6 +33,7 @@ QSA_DEVERR_ROWS = 0x4
 QSA_DEVERR_Q_RANGE = 0x8
 QSA_DEVERR_SELECTED = 0x10
 QSA_DEVERR_SLOT = 0x20
+QSA_KV_NVFP4, QSA_KV_FP8 = 0, 1
 QSA_MAX_PLANES = 16
 
 # every symbol that include/qsa.h declares
@@ -65,6 +66,7 @@ class Shape(ctypes.Structure):
         ("topk", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
+        ("kv_format", ctypes.c_int32),
     ]
 
 
@@ -120,8 +122,8 @@ def lib() -> ctypes.CDLL:
         L.qsa_select_topk.argtypes = [sp, pp, P, P, P]
         L.qsa_workspace_bytes.argtypes = [sp, I32]
         L.qsa_workspace_bytes.restype = SZ
-        L.qsa_sparse_decode.argtypes = [sp, pp, P, P, P, P, I32, P, SZ, P]
-        L.qsa_select_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, I32, P, SZ, P]
+        L.qsa_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, I32, P, SZ, P]
+        L.qsa_select_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, P, I32, P, SZ, P]
         L.qsa_kv_store.argtypes = [sp, pp, P, P, P]
         L.qsa_nvfp4_dequant_pages.argtypes = [sp, P, P, ctypes.c_float, P, I32, P, P]
         plp = ctypes.POINTER(Plane)
@@ -186,21 +188,22 @@ def qsa_workspace_bytes(shape: Shape, num_splits: int = 0) -> int:
 
 
 def qsa_sparse_decode(shape: Shape, paged: Paged, q, selected, out, lse=None, num_splits: int = 0,
-                      workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+                      workspace=None, workspace_bytes: Optional[int] = None, stream=None, gate=None) -> None:
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qsa_sparse_decode(ctypes.byref(shape), ctypes.byref(paged), _ptr(q), _ptr(selected), _ptr(out),
-                                   _ptr(lse), int(num_splits), _ptr(workspace), int(workspace_bytes),
+                                   _ptr(lse), _ptr(gate), int(num_splits), _ptr(workspace), int(workspace_bytes),
                                    _stream(stream)), "qsa_sparse_decode")
 
 
 def qsa_select_sparse_decode(shape: Shape, paged: Paged, q, scores, selected, out, lse=None, num_splits: int = 0,
-                             workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+                             workspace=None, workspace_bytes: Optional[int] = None, stream=None, gate=None) -> None:
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qsa_select_sparse_decode(ctypes.byref(shape), ctypes.byref(paged), _ptr(q), _ptr(scores),
-                                          _ptr(selected), _ptr(out), _ptr(lse), int(num_splits), _ptr(workspace),
-                                          int(workspace_bytes), _stream(stream)), "qsa_select_sparse_decode")
+                                          _ptr(selected), _ptr(out), _ptr(lse), _ptr(gate), int(num_splits),
+                                          _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "qsa_select_sparse_decode")
 
 
 def qsa_kv_store(shape: Shape, paged: Paged, new_k, new_v, stream=None) -> None:

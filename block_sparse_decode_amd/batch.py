@@ -54,6 +54,7 @@ class DeviceBatch:
     sm_scale: float
     k_global: float = 1.0
     v_global: float = 1.0
+    kv_format: int = 0              # QSA_KV_NVFP4 or QSA_KV_FP8
 
     @staticmethod
     def upload(w, device="cuda") -> "DeviceBatch":
@@ -69,7 +70,8 @@ class DeviceBatch:
             num_requests=int(w.B), num_rows=int(w.N), max_rows=max(1, int(w.max_rows)),
             q_heads=c.q_heads, kv_heads=c.kv_heads, head_dim=c.head_dim, page_size=c.page_size,
             max_pages=int(w.MP), num_phys_pages=int(w.NP), topk=c.topk, window=c.window,
-            sm_scale=float(w.sm_scale), k_global=float(c.k_global), v_global=float(c.v_global))
+            sm_scale=float(w.sm_scale), k_global=float(c.k_global), v_global=float(c.v_global),
+            kv_format=1 if getattr(c, "kv_format", "nvfp4") == "fp8" else 0)
 
     @property
     def kw(self) -> int:
@@ -78,7 +80,7 @@ class DeviceBatch:
     def shape(self) -> Shape:
         return Shape(self.num_requests, self.num_rows, self.max_rows, self.q_heads, self.kv_heads,
                      self.head_dim, self.page_size, self.max_pages, self.num_phys_pages, self.topk,
-                     self.window, self.sm_scale)
+                     self.window, self.sm_scale, self.kv_format)
 
     def paged(self, error_word: bool = True) -> Paged:
         return Paged(self.page_table.data_ptr(), self.seq_lens.data_ptr(), self.row_offsets.data_ptr(),
@@ -93,6 +95,8 @@ class DeviceBatch:
         out = []
         for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales):
             NP, Hkv, P, nb = t.shape
+            if nb == 0:
+                continue                      # the FP8 cache has no scale planes
             out.append(Plane(t.data_ptr(), t.numel(), Hkv * P * nb, nb, P * nb, nb, Hkv, NP, P, 0))
         NP, Hkv, d = self.index_keys.shape
         out.append(Plane(self.index_keys.data_ptr(), self.index_keys.numel() * 2, Hkv * d * 2, 0, d * 2, d * 2, Hkv,
@@ -128,8 +132,10 @@ class Step:
     The argument blocks and outputs are built once, so a call only launches kernels.
     """
 
-    def __init__(self, batch: DeviceBatch, num_splits: int = 0, with_lse: bool = True, fused: bool = True):
+    def __init__(self, batch: DeviceBatch, num_splits: int = 0, with_lse: bool = True, fused: bool = True,
+                 gate=None):
         self.b = batch
+        self.gate = gate
         self.fused = fused
         self.num_splits = num_splits
         self.shape_ = batch.shape()
@@ -150,8 +156,8 @@ class Step:
         ws = self.ws
         self._a_scores = (sh, pg, self.b.q.data_ptr(), self.scores.data_ptr())
         self._a_fused = (sh, pg, self.b.q.data_ptr(), self.scores.data_ptr(), self.selected.data_ptr(),
-                         self.out.data_ptr(), None if self.lse is None else self.lse.data_ptr(), int(num_splits),
-                         ws.data_ptr(), ws.numel())
+                         self.out.data_ptr(), None if self.lse is None else self.lse.data_ptr(),
+                         None if gate is None else gate.data_ptr(), int(num_splits), ws.data_ptr(), ws.numel())
 
     def _raw(self, fn, args, stream, name):
         import torch
@@ -168,7 +174,7 @@ class Step:
 
     def decode_call(self, stream=None, selected=None):
         qsa_sparse_decode(self.shape_, self.paged_, self.b.q, self.selected if selected is None else selected,
-                          self.out, self.lse, self.num_splits, self.ws, None, stream)
+                          self.out, self.lse, self.num_splits, self.ws, None, stream, gate=self.gate)
 
     def select_decode_call(self, stream=None):
         self._raw(self._L.qsa_select_sparse_decode, self._a_fused, stream, "qsa_select_sparse_decode")

@@ -34,6 +34,7 @@ qsa_status check_shape(const qsa_shape *sh)
     if ((int64_t)sh->topk + sh->window > kMaxKW) return QSA_ERR_UNSUPPORTED;
     if (sh->num_requests > 65535 || sh->num_kv_heads > 65535) return QSA_ERR_UNSUPPORTED;
     if (sh->num_rows > (int64_t)sh->num_requests * sh->max_rows_per_request) return QSA_ERR_INVALID_ARG;
+    if (sh->kv_format != QSA_KV_NVFP4 && sh->kv_format != QSA_KV_FP8) return QSA_ERR_INVALID_ARG;
     return QSA_OK;
 }
 
@@ -208,8 +209,8 @@ namespace {
 // Shared by qsa_sparse_decode (scores == NULL: `selected` is an input) and
 // qsa_select_sparse_decode (the selection is computed from `scores` and written to `selected`).
 qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const float *scores,
-                       int32_t *selected, uint16_t *out, float *lse, int32_t num_splits, void *workspace,
-                       size_t workspace_bytes, void *stream)
+                       int32_t *selected, uint16_t *out, float *lse, const uint16_t *gate, int32_t num_splits,
+                       void *workspace, size_t workspace_bytes, void *stream)
 {
     qsa_status st = check_shape(sh);
     if (st != QSA_OK) return st;
@@ -217,14 +218,16 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     if (sh->max_rows_per_request * (sh->num_q_heads / sh->num_kv_heads) > kMaxCols) return QSA_ERR_UNSUPPORTED;
     if (num_splits < 0) return QSA_ERR_INVALID_ARG;
     if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
-    if (!q || !out || !pg->page_table || !pg->k_codes || !pg->k_scales || !pg->v_codes || !pg->v_scales)
+    const bool nvfp4 = sh->kv_format == QSA_KV_NVFP4;
+    if (!q || !out || !pg->page_table || !pg->k_codes || !pg->v_codes) return QSA_ERR_INVALID_ARG;
+    if (nvfp4 && (!pg->k_scales || !pg->v_scales || !aligned16(pg->k_scales) || !aligned16(pg->v_scales)))
         return QSA_ERR_INVALID_ARG;
     const bool fused = scores != nullptr;
     const int KW = sh->topk + sh->window;
     if (KW > 0 && !selected) return QSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out) || !aligned16(pg->page_table) || !aligned16(pg->k_codes) ||
-        !aligned16(pg->k_scales) || !aligned16(pg->v_codes) || !aligned16(pg->v_scales) ||
-        (selected && !aligned16(selected)) || (lse && !aligned16(lse)) || (fused && !aligned16(scores)))
+        !aligned16(pg->v_codes) || (selected && !aligned16(selected)) || (lse && !aligned16(lse)) ||
+        (fused && !aligned16(scores)) || (gate && !aligned16(gate)))
         return QSA_ERR_INVALID_ARG;
     if (!isfinite(pg->k_global) || !isfinite(pg->v_global)) return QSA_ERR_INVALID_ARG;
     // the logit scale sm_scale * k_global * log2(e) must be a positive normal fp32: the
@@ -272,6 +275,8 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     prm.tiles = (int)decode_tiles(sh);
     prm.qk_scale_log2 = (float)qk;
     prm.v_global = pg->v_global;
+    prm.gate = gate;
+    prm.kv_format = sh->kv_format;
     hipError_t e;
     if (!fused || KW == 0) {
         e = launch_sparse_decode(prm, sh->head_dim, (hipStream_t)stream);
@@ -303,20 +308,20 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
 extern "C" {
 
 qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const int32_t *selected,
-                             uint16_t *out, float *lse, int32_t num_splits, void *workspace, size_t workspace_bytes,
-                             void *stream)
+                             uint16_t *out, float *lse, const uint16_t *gate, int32_t num_splits, void *workspace,
+                             size_t workspace_bytes, void *stream)
 {
-    return decode_call(sh, pg, q, nullptr, const_cast<int32_t *>(selected), out, lse, num_splits, workspace,
+    return decode_call(sh, pg, q, nullptr, const_cast<int32_t *>(selected), out, lse, gate, num_splits, workspace,
                        workspace_bytes, stream);
 }
 
 qsa_status qsa_select_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const float *scores,
-                                    int32_t *selected, uint16_t *out, float *lse, int32_t num_splits,
-                                    void *workspace, size_t workspace_bytes, void *stream)
+                                    int32_t *selected, uint16_t *out, float *lse, const uint16_t *gate,
+                                    int32_t num_splits, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (sh && pg && sh->topk + sh->window > 0 && !scores && sh->num_rows > 0 && sh->num_requests > 0)
         return QSA_ERR_INVALID_ARG;
-    return decode_call(sh, pg, q, scores, selected, out, lse, num_splits, workspace, workspace_bytes, stream);
+    return decode_call(sh, pg, q, scores, selected, out, lse, gate, num_splits, workspace, workspace_bytes, stream);
 }
 
 qsa_status qsa_kv_store(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *new_k, const uint16_t *new_v,
@@ -324,6 +329,7 @@ qsa_status qsa_kv_store(const qsa_shape *sh, const qsa_paged *pg, const uint16_t
 {
     qsa_status st = check_shape(sh);
     if (st != QSA_OK) return st;
+    if (sh->kv_format != QSA_KV_NVFP4) return QSA_ERR_UNSUPPORTED;
     if ((st = check_rows_ptrs(pg)) != QSA_OK) return st;
     if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
     if (!new_k || !new_v || !pg->page_table || !pg->k_codes || !pg->k_scales || !pg->v_codes || !pg->v_scales ||

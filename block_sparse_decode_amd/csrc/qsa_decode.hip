@@ -53,29 +53,51 @@ __device__ __forceinline__ void wave_lds_fence()
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D>
+// Cache formats: NVFP4 (e2m1 codes, two per byte, plus one e4m3 scale per 16 elements) and
+// FP8 (one e4m3 byte per element, unit scales).
+constexpr int kNvfp4 = 0, kFp8 = 1;
+
+template <int D, int F>
+constexpr int code_bytes() { return F == kFp8 ? D : D / 2; }       // per token and KV head
+template <int D, int F>
+constexpr int scale_bytes() { return F == kFp8 ? 0 : D / 16; }
+
+template <int D, int F>
 struct RawTile;   // one lane's share of a 16-token M-tile: its d/4 consecutive elements
 
 template <>
-struct RawTile<128> {
+struct RawTile<128, kNvfp4> {
     uint4 codes;        // 32 e2m1 codes
     uint32_t scales;    // 2 e4m3 bytes in the low half
 };
 
 template <>
-struct RawTile<64> {
+struct RawTile<64, kNvfp4> {
     uint2 codes;        // 16 e2m1 codes
     uint32_t scales;    // 1 e4m3 byte
+};
+
+template <>
+struct RawTile<128, kFp8> {
+    uint4 lo, hi;       // 32 e4m3 bytes
+};
+
+template <>
+struct RawTile<64, kFp8> {
+    uint4 lo;           // 16 e4m3 bytes
 };
 
 // `codes` / `scales`: the sub-chunk's first token (wave-uniform); `co` / `so`: this lane's
 // byte offsets from there (token li of the M-tile, chunk gq), so each load is a uniform
 // 64-bit base plus a 32-bit lane offset with no per-load vector address arithmetic.
-template <int D>
-__device__ __forceinline__ RawTile<D> load_raw(const uint8_t *codes, const uint8_t *scales, uint32_t co, uint32_t so)
+template <int D, int F>
+__device__ __forceinline__ RawTile<D, F> load_raw(const uint8_t *codes, const uint8_t *scales, uint32_t co, uint32_t so)
 {
-    RawTile<D> t;
-    if constexpr (D == 128) {
+    RawTile<D, F> t;
+    if constexpr (F == kFp8) {
+        t.lo = *reinterpret_cast<const uint4 *>(codes + co);
+        if constexpr (D == 128) t.hi = *reinterpret_cast<const uint4 *>(codes + co + 16);
+    } else if constexpr (D == 128) {
         t.codes = *reinterpret_cast<const uint4 *>(codes + co);
         t.scales = *reinterpret_cast<const uint16_t *>(scales + so);
     } else {
@@ -86,7 +108,7 @@ __device__ __forceinline__ RawTile<D> load_raw(const uint8_t *codes, const uint8
 }
 
 template <int D>
-__device__ __forceinline__ uint32_t raw_dword(const RawTile<D> &t, int i)
+__device__ __forceinline__ uint32_t raw_dword(const RawTile<D, kNvfp4> &t, int i)
 {
     if constexpr (D == 128) {
         return i == 0 ? t.codes.x : i == 1 ? t.codes.y : i == 2 ? t.codes.z : t.codes.w;
@@ -95,27 +117,59 @@ __device__ __forceinline__ uint32_t raw_dword(const RawTile<D> &t, int i)
     }
 }
 
-// Dequantise a lane's 8-element group i (elements 8i..8i+7 of its d/4 chunk); `sc` holds
-// the chunk's block scales as f16 ({s0, s1} for d = 128, {s0, -} for d = 64).
-template <int D>
-__device__ __forceinline__ f16x8 dequant_group(const RawTile<D> &t, f16x2 sc, int i)
+// Eight e4m3 bytes (two dwords) -> eight f16 values, exactly (every E4M3FN value is an f16
+// value); the scaled convert applies only its scale's exponent, so scale 1.0 is a plain decode.
+__device__ __forceinline__ f16x8 fp8x8_to_f16x8(uint32_t a, uint32_t b)
 {
-    return nvfp4_dequant8(raw_dword<D>(t, i), (D == 128 && i >= 2) ? sc.y : sc.x);
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, false);
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a, 1.0f, true);
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, true);
+    return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                   __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int D>
-__device__ __forceinline__ void load_unit(const DecodeParams &prm, int phys, int g, int c, uint32_t co, uint32_t so,
-                                          RawTile<D> (&kr)[2], RawTile<D> (&vr)[2])
+// Dequantise a lane's 8-element group i (elements 8i..8i+7 of its d/4 chunk); for NVFP4 `sc`
+// holds the chunk's block scales as f16 ({s0, s1} for d = 128, {s0, -} for d = 64).
+template <int D, int F>
+__device__ __forceinline__ f16x8 dequant_group(const RawTile<D, F> &t, f16x2 sc, int i)
 {
+    if constexpr (F == kFp8) {
+        if constexpr (D == 128) {
+            const uint4 &h = i < 2 ? t.lo : t.hi;
+            return (i & 1) ? fp8x8_to_f16x8(h.z, h.w) : fp8x8_to_f16x8(h.x, h.y);
+        } else {
+            return (i & 1) ? fp8x8_to_f16x8(t.lo.z, t.lo.w) : fp8x8_to_f16x8(t.lo.x, t.lo.y);
+        }
+    } else {
+        return nvfp4_dequant8(raw_dword<D>(t, i), (D == 128 && i >= 2) ? sc.y : sc.x);
+    }
+}
+
+template <int D, int F>
+__device__ __forceinline__ f16x2 tile_scales(const RawTile<D, F> &t)
+{
+    if constexpr (F == kFp8) {
+        return (f16x2){(half_t)1.0f, (half_t)1.0f};
+    } else {
+        return e4m3x2_to_f16x2(t.scales);
+    }
+}
+
+template <int D, int F>
+__device__ __forceinline__ void load_unit(const DecodeParams &prm, int phys, int g, int c, uint32_t co, uint32_t so,
+                                          RawTile<D, F> (&kr)[2], RawTile<D, F> (&vr)[2])
+{
+    constexpr int CB = code_bytes<D, F>(), SB = scale_bytes<D, F>();
     // the sub-chunk's first token in the pool (phys, g and c are wave-uniform)
     const int64_t tok = ((int64_t)phys * prm.Hkv + g) * prm.P + c * 32;
-    const uint8_t *kc = prm.k_codes + tok * (D / 2), *ks = prm.k_scales + tok * (D / 16);
-    const uint8_t *vc = prm.v_codes + tok * (D / 2), *vsc = prm.v_scales + tok * (D / 16);
+    const uint8_t *kc = prm.k_codes + tok * CB, *vc = prm.v_codes + tok * CB;
+    const uint8_t *ks = SB ? prm.k_scales + tok * SB : nullptr, *vsc = SB ? prm.v_scales + tok * SB : nullptr;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        const uint32_t cm = co + mt * 16 * (D / 2), sm = so + mt * 16 * (D / 16);
-        kr[mt] = load_raw<D>(kc, ks, cm, sm);
-        vr[mt] = load_raw<D>(vc, vsc, cm, sm);
+        const uint32_t cm = co + mt * 16 * CB, sm = so + mt * 16 * SB;
+        kr[mt] = load_raw<D, F>(kc, ks, cm, sm);
+        vr[mt] = load_raw<D, F>(vc, vsc, cm, sm);
     }
 }
 
@@ -160,7 +214,7 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
 
 // SELC = 0: the rows' selections are an input. SELC = 8 or 16: they are computed here from
 // the scores (select_row with that many columns per lane) and also written out.
-template <int D, int SELC>
+template <int D, int SELC, int F>
 __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(DecodeParams prm)
 {
     constexpr int NW = kDecodeWaves;
@@ -381,14 +435,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
                         (half_t)1.0f, (half_t)1.0f, (half_t)1.0f, (half_t)1.0f};
     const int trow = 4 * gq + (li >> 2);            // transposed-read rows trow, trow + 16
     // this lane's byte offsets inside a sub-chunk's codes and scales (token li, chunk gq)
-    const uint32_t lco = (uint32_t)(li * (D / 2) + gq * (D / 8));
-    const uint32_t lso = (uint32_t)(li * (D / 16) + gq * (D / 64));
+    const uint32_t lco = (uint32_t)(li * code_bytes<D, F>() + gq * (code_bytes<D, F>() / 4));
+    const uint32_t lso = (uint32_t)(li * scale_bytes<D, F>() + gq * (scale_bytes<D, F>() / 4));
 
     // One register set: a sub-chunk's raw codes are consumed (K into the MFMA operands, V into
     // LDS) before the next sub-chunk's loads are issued into the same registers; those loads
     // are then in flight during the softmax and the P.V products.
-    RawTile<D> kr[2], vr[2];
-    auto process = [&](const UnitCursor &u, const UnitCursor &un, RawTile<D>(&kr)[2], RawTile<D>(&vr)[2]) {
+    RawTile<D, F> kr[2], vr[2];
+    auto process = [&](const UnitCursor &u, const UnitCursor &un, RawTile<D, F>(&kr)[2], RawTile<D, F>(&vr)[2]) {
         const int p = (int)(u.pm & 0xffffu);
         const uint32_t rmask = (u.pm >> 16) & 0xffu;
 
@@ -396,27 +450,27 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         f32x4 sacc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const f16x2 ksc = e4m3x2_to_f16x2(kr[mt].scales);
+            const f16x2 ksc = tile_scales<D, F>(kr[mt]);
             sacc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_group<D>(kr[mt], ksc, ks), q_lds[ks][lane],
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_group<D, F>(kr[mt], ksc, ks), q_lds[ks][lane],
                                                                   sacc[mt], 0, 0, 0);
         }
 
         // V -> LDS, token-major rows of this 32-token sub-chunk (16-byte chunks swizzled)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const f16x2 vsc = e4m3x2_to_f16x2(vr[mt].scales);
+            const f16x2 vsc = tile_scales<D, F>(vr[mt]);
             const int row = mt * 16 + li;
 #pragma unroll
             for (int i = 0; i < DQ / 8; ++i) {
                 const int ch = gq * (DQ / 8) + i;
                 *reinterpret_cast<f16x8 *>(vs + row * D + ((ch ^ vswz(row)) & (D / 8 - 1)) * 8) =
-                    dequant_group<D>(vr[mt], vsc, i);
+                    dequant_group<D, F>(vr[mt], vsc, i);
             }
         }
-        if (un.have) load_unit<D>(prm, un.phys, g, un.c, lco, lso, kr, vr);
+        if (un.have) load_unit<D, F>(prm, un.phys, g, un.c, lco, lso, kr, vr);
 
         // online softmax with a lazily raised column max; P stays in registers
         const int tok0 = (p << prm.log2P) + u.c * 32;                  // wave-uniform
@@ -474,7 +528,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     };
 
     UnitCursor u = seek_unit(u_lo + wave, u_hi, lc, u_pm, u_phys);
-    if (u.have) load_unit<D>(prm, u.phys, g, u.c, lco, lso, kr, vr);
+    if (u.have) load_unit<D, F>(prm, u.phys, g, u.c, lco, lso, kr, vr);
     while (u.have) {
         const UnitCursor un = seek_unit(u.u + NW, u_hi, lc, u_pm, u_phys);
         process(u, un, kr, vr);
@@ -583,7 +637,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     const float sc = (L > 0.0f) ? prm.v_global / L : 0.0f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-        const f32x4 o = oacc[dt] * sc;
+        f32x4 o = oacc[dt] * sc;
+        if (prm.gate) {
+            // the gated epilogue: out * sigmoid(gate), one rounding to bf16 after the product
+            const uint2 gr = *reinterpret_cast<const uint2 *>(prm.gate + ((int64_t)row * prm.Hq + head) * D +
+                                                                dt * 16 + gq * 4);
+            const float gv[4] = {bf16lo(gr.x), bf16hi(gr.x), bf16lo(gr.y), bf16hi(gr.y)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv[i]));
+        }
         uint2 packed;
         packed.x = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
         packed.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
@@ -598,7 +661,10 @@ static hipError_t launch_decode_d(const DecodeParams &prm, hipStream_t stream)
 {
     const int64_t per = ((int64_t)prm.tiles * prm.splits + kXcds - 1) / kXcds;   // work items per XCD
     const unsigned grid = (unsigned)(per * kXcds);
-    sparse_decode_kernel<D, SELC><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+    if (prm.kv_format == kFp8)
+        sparse_decode_kernel<D, SELC, kFp8><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+    else
+        sparse_decode_kernel<D, SELC, kNvfp4><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
     return hipGetLastError();
 }
 

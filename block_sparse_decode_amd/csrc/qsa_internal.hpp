@@ -52,6 +52,8 @@ struct DecodeParams {
     int k, W;                 // selection fused in only
     float qk_scale_log2;      // sm_scale * k_global * log2(e)
     float v_global;
+    const uint16_t *gate;     // optional bf16 [N][Hq][d]: out = o * sigmoid(gate)
+    int kv_format;            // QSA_KV_NVFP4 or QSA_KV_FP8
 };
 
 struct StoreParams {

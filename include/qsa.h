@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 
 typedef enum qsa_status {
     QSA_OK = 0,
@@ -69,7 +69,15 @@ typedef struct qsa_shape {
     int32_t topk;                  /* k >= 0 */
     int32_t window;                /* W >= 0, k + W <= 256 */
     float   sm_scale;              /* softmax scale, normally (float)(1 / sqrt(d)) */
+    int32_t kv_format;             /* QSA_KV_NVFP4 (0) or QSA_KV_FP8 (1): the K/V pools' format */
 } qsa_shape;
+
+/* K/V pool formats (qsa_shape.kv_format). NVFP4: the layout of qsa_paged below. FP8 (PR
+   #20937, the FP8 KV cache of its tested configurations, unit scales): k_codes / v_codes
+   are uint8 [NP][Hkv][P][d], one OCP E4M3FN byte per element, K = e4m3 * k_global; the
+   scale planes are not read (may be NULL). Only the attention calls take FP8 pools. */
+#define QSA_KV_NVFP4 0
+#define QSA_KV_FP8   1
 
 /*
  * The paged KV cache. One physical page index addresses every plane (PR #20276, Features,
@@ -152,6 +160,9 @@ size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
  *                                    a page listed twice counts once)
  *   out        bf16  [N][Hq][d]     (device, written in full, RNE)
  *   lse        fp32  [N][Hq]        (device, optional: natural-log sum of exp of the logits)
+ *   gate       bf16  [N][Hq][d]     (device, optional, 16-byte aligned: the gated epilogue of
+ *                                    PR #20937's verify kernel, out = bf16(o * sigmoid(gate)),
+ *                                    o the attention in fp32; lse is not gated)
  *   num_splits 0 = the library's choice; > 0 forces that many KV splits per
  *              (request, KV head), clamped to 64
  *   workspace  device scratch of at least qsa_workspace_bytes(shape, num_splits) bytes,
@@ -159,7 +170,7 @@ size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
  * For row j of request b and q head h, the tokens attended are
  *   T = {(p, t): p listed in the row, page_table[b][p] valid, t < P, p * P + t < L}.
  * The output is softmax(sm_scale * k_global * q . K_raw) @ (v_global * V_raw) over T, where
- * K_raw and V_raw are e2m1 * e4m3. An empty T gives out = 0 and lse = -inf. Each request's
+ * K_raw and V_raw are e2m1 * e4m3 (NVFP4) or e4m3 (FP8). An empty T gives out = 0 and lse = -inf. Each request's
  * rows share one read of the union of their selected pages. fp32 accumulation; the q and
  * P operands of the MFMA tiles are f16 (q must lie in the f16 range; see QSA_DEVERR_Q_RANGE).
  * Deterministic for a fixed num_splits. sm_scale * k_global * log2(e) must be a positive
@@ -167,7 +178,7 @@ size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
  */
 qsa_status qsa_sparse_decode(const qsa_shape *shape, const qsa_paged *paged,
                              const uint16_t *q, const int32_t *selected,
-                             uint16_t *out, float *lse, int32_t num_splits,
+                             uint16_t *out, float *lse, const uint16_t *gate, int32_t num_splits,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -182,7 +193,7 @@ qsa_status qsa_sparse_decode(const qsa_shape *shape, const qsa_paged *paged,
  */
 qsa_status qsa_select_sparse_decode(const qsa_shape *shape, const qsa_paged *paged,
                                     const uint16_t *q, const float *scores, int32_t *selected,
-                                    uint16_t *out, float *lse, int32_t num_splits,
+                                    uint16_t *out, float *lse, const uint16_t *gate, int32_t num_splits,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert q.qsa_abi_version() == 1
+    assert q.qsa_abi_version() == 2
     for st, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
                      (3, "workspace too small"), (4, "HIP launch error"), (99, "unknown status")]:
         assert q.qsa_status_string(st) == text
@@ -86,6 +86,13 @@ def _raw(name, *args):
     return getattr(q.lib(), name)(*args)
 
 
+def _rawd(name, *args):
+    """The attention calls without a gate: None goes in the gate position (after lse)."""
+    args = list(args)
+    args.insert(6 if name == "qsa_sparse_decode" else 7, None)
+    return _raw(name, *args)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), 2), (dict(head_dim=256), 2), (dict(page_size=32), 2), (dict(max_pages=4097), 2),
     (dict(topk=250, window=7), 2), (dict(max_rows_per_request=5), 2),
@@ -97,7 +104,7 @@ def test_shape_validation(kw, status):
     pg = _paged()
     assert _raw("qsa_index_scores", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, None) == status
     assert _raw("qsa_select_topk", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, None) == status
-    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
                 1 << 30, None) == status
     assert q.qsa_workspace_bytes(sh, 0) == 0
 
@@ -109,43 +116,66 @@ def test_pointer_validation():
     assert _raw("qsa_index_scores", ctypes.byref(sh), None, FAKE, FAKE, None) == 1
     assert _raw("qsa_index_scores", ctypes.byref(sh), ctypes.byref(pg), None, FAKE, None) == 1
     assert _raw("qsa_select_topk", ctypes.byref(sh), ctypes.byref(pg), FAKE, None, None) == 1
-    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(v_codes=None)), FAKE, FAKE, FAKE,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(v_codes=None)), FAKE, FAKE, FAKE,
                 None, 0, FAKE, 1 << 30, None) == 1
     # misaligned tensors
     assert _raw("qsa_index_scores", ctypes.byref(sh), ctypes.byref(pg), FAKE + 2, FAKE, None) == 1
-    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(k_codes=FAKE + 8)), FAKE, FAKE, FAKE,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(k_codes=FAKE + 8)), FAKE, FAKE, FAKE,
                 None, 0, FAKE, 1 << 30, None) == 1
     # negative split count, non-finite global scale
-    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, -1, FAKE,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, -1, FAKE,
                 1 << 30, None) == 1
-    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(k_global=float("nan"))), FAKE, FAKE,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(_paged(k_global=float("nan"))), FAKE, FAKE,
                 FAKE, None, 0, FAKE, 1 << 30, None) == 1
     # the logit scale sm_scale * k_global must be positive
     for bad_sh, bad_pg in ((_shape(sm_scale=0.0), pg), (_shape(sm_scale=-0.1), pg), (sh, _paged(k_global=-1.0)),
                            (sh, _paged(k_global=0.0))):
-        assert _raw("qsa_sparse_decode", ctypes.byref(bad_sh), ctypes.byref(bad_pg), FAKE, FAKE, FAKE, None, 0,
+        assert _rawd("qsa_sparse_decode", ctypes.byref(bad_sh), ctypes.byref(bad_pg), FAKE, FAKE, FAKE, None, 0,
                     FAKE, 1 << 30, None) == 1
-        assert _raw("qsa_select_sparse_decode", ctypes.byref(bad_sh), ctypes.byref(bad_pg), FAKE, FAKE, FAKE,
+        assert _rawd("qsa_select_sparse_decode", ctypes.byref(bad_sh), ctypes.byref(bad_pg), FAKE, FAKE, FAKE,
                     FAKE, None, 0, FAKE, 1 << 30, None) == 1
     # too many q columns per request (4 rows x 32 heads per KV head)
     big = _shape(num_q_heads=128)
-    assert _raw("qsa_sparse_decode", ctypes.byref(big), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(big), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
                 1 << 30, None) == 2
+
+
+def test_kv_format_and_gate_validation():
+    pg = _paged()
+    # an unknown format is refused by every call that takes a shape
+    bad = _shape(kv_format=2)
+    assert _raw("qsa_index_scores", ctypes.byref(bad), ctypes.byref(pg), FAKE, FAKE, None) == 1
+    assert _rawd("qsa_sparse_decode", ctypes.byref(bad), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
+                 1 << 30, None) == 1
+    # FP8 pools: the scale planes are not needed; the store does not take FP8 pools
+    fp8 = _shape(kv_format=1)
+    no_scales = _paged(k_scales=None, v_scales=None)
+    assert _raw("qsa_kv_store", ctypes.byref(fp8), ctypes.byref(pg), FAKE, FAKE, None) == 2
+    assert _rawd("qsa_sparse_decode", ctypes.byref(_shape()), ctypes.byref(no_scales), FAKE, FAKE, FAKE, None, 0,
+                 FAKE, 1 << 30, None) == 1                       # NVFP4 needs them
+    assert _rawd("qsa_sparse_decode", ctypes.byref(fp8), ctypes.byref(no_scales), FAKE, FAKE, FAKE, None, -1,
+                 FAKE, 1 << 30, None) == 1                       # (refused later, on the split count)
+    # a gate must be 16-byte aligned
+    sh = _shape()
+    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, FAKE + 2, 0, FAKE,
+                1 << 30, None) == 1
+    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, None,
+                FAKE + 8, 0, FAKE, 1 << 30, None) == 1
 
 
 def test_fused_select_decode_validation():
     sh, pg = _shape(), _paged()
     # the selection needs the scores and somewhere to write the rows
-    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, None, FAKE, FAKE, None, 0,
+    assert _rawd("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, None, FAKE, FAKE, None, 0,
                 FAKE, 1 << 30, None) == 1
-    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, None, FAKE, None, 0,
+    assert _rawd("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, None, FAKE, None, 0,
                 FAKE, 1 << 30, None) == 1
-    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE + 4, FAKE, FAKE, None,
+    assert _rawd("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE + 4, FAKE, FAKE, None,
                 0, FAKE, 1 << 30, None) == 1
     # the checks of qsa_sparse_decode apply
-    assert _raw("qsa_select_sparse_decode", ctypes.byref(_shape(head_dim=96)), ctypes.byref(pg), FAKE, FAKE, FAKE,
+    assert _rawd("qsa_select_sparse_decode", ctypes.byref(_shape(head_dim=96)), ctypes.byref(pg), FAKE, FAKE, FAKE,
                 FAKE, None, 0, FAKE, 1 << 30, None) == 2
-    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, None, 4,
+    assert _rawd("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, FAKE, None, 4,
                 FAKE, q.qsa_workspace_bytes(sh, 4) - 1, None) == 3
 
 
@@ -262,9 +292,9 @@ def test_workspace_sizing():
     assert q.qsa_workspace_bytes(sh, 1000) == q.qsa_workspace_bytes(sh, 64)
     # a too-small workspace is refused before any launch
     pg = _paged()
-    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 4, FAKE,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 4, FAKE,
                 q.qsa_workspace_bytes(sh, 4) - 1, None) == 3
-    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 4, None,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 4, None,
                 1 << 30, None) == 3
 
 
@@ -273,9 +303,9 @@ def test_empty_batches_are_no_ops():
     pg = _paged()
     assert _raw("qsa_index_scores", ctypes.byref(sh), ctypes.byref(pg), None, None, None) == 0
     assert _raw("qsa_select_topk", ctypes.byref(sh), ctypes.byref(pg), None, None, None) == 0
-    assert _raw("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), None, None, None, None, 0, None, 0,
+    assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), None, None, None, None, 0, None, 0,
                 None) == 0
-    assert _raw("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), None, None, None, None, None, 0,
+    assert _rawd("qsa_select_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), None, None, None, None, None, 0,
                 None, 0, None) == 0
     dq = _shape()
     assert _raw("qsa_nvfp4_dequant_pages", ctypes.byref(dq), None, None, ctypes.c_float(1.0), None, 0, None,
