@@ -118,7 +118,8 @@ def algorithmic_bytes(w, selected):
     c = w.cfg
     P, d, Hq, Hkv = c.page_size, c.head_dim, c.q_heads, c.kv_heads
     KW = c.topk + c.window
-    page_bytes = P * (d // 2 + d // 16) * 2          # K + V of one (page, KV head)
+    fp8 = getattr(c, "kv_format", "nvfp4") == "fp8"
+    page_bytes = P * (d if fp8 else d // 2 + d // 16) * 2       # K + V of one (page, KV head)
     attn_kv = 0
     pt_entries = 0
     index_keys = 0
@@ -340,6 +341,37 @@ def main():
     gather_us = stage_us(gather)
     restore_us = stage_us(restore)
     row_bytes = sum(pl.nseg * pl.seg_bytes for pl in steps[0].b.rollback_planes())
+
+    # (5) the attention variants: the gated epilogue (same pools), and FP8 pools (unit-scale
+    # E4M3, two layers of the same workload re-encoded)
+    gen = np.random.default_rng(1)
+    gate = torch.from_numpy(synth.bf16_bits_from_f32(gen.standard_normal(w.q.shape, dtype=np.float32)).view(
+        np.int16)).to(dev)
+    gsteps = {id(st): Step(st.b, num_splits=args.splits, gate=gate) for st in steps}
+    gated_us = stage_us(lambda st: gsteps[id(st)].select_decode_call(stream))
+    w8 = synth.generate(w.cfg.with_(kv_format="fp8", name=w.cfg.name + "_fp8"))
+    base8 = DeviceBatch.upload(w8, dev)
+    layers8 = [base8]
+    b8 = DeviceBatch(**{**base8.__dict__})
+    for name in ("k_codes", "k_scales", "v_codes", "v_scales", "index_keys"):
+        setattr(b8, name, getattr(base8, name).clone())
+    layers8.append(b8)
+    steps8 = [Step(b, num_splits=args.splits) for b in layers8]
+    for st in steps8:
+        st(stream)
+    torch.cuda.synchronize()
+    sel8 = steps8[0].selected.cpu().numpy()
+
+    def stage8_us(fn):
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(K):
+            fn(steps8[i % 2])
+        b2.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b2) * 1e3 / K
+    fp8_us = stage8_us(lambda st: st.select_decode_call(stream))
+    fp8_bytes = algorithmic_bytes(w8, sel8)["select_attention"]
     err = int(base.error_word[0].item())
 
     ab = algorithmic_bytes(w, sel)
@@ -375,6 +407,9 @@ def main():
                    "kv_store_us": round(store_us, 2),
                    "kv_store_gbs": round(ab["kv_store"] / (store_us * 1e-6) / 1e9, 1),
                    "rollback_gather_us": round(gather_us, 2), "rollback_restore_us": round(restore_us, 2),
+                   "gated_select_sparse_decode_us": round(gated_us, 2),
+                   "fp8_select_sparse_decode_us": round(fp8_us, 2),
+                   "fp8_select_attention_gbs": round(fp8_bytes / (fp8_us * 1e-6) / 1e9, 1),
                    "timing": "mean of back-to-back launches between one HIP event pair on the launch stream"},
         "bytes": ab,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -174,10 +174,13 @@ __device__ __forceinline__ void load_unit(const DecodeParams &prm, int phys, int
 }
 
 // V staging in LDS: row t (token) holds D f16 values as D/8 chunks of 16 bytes; chunk ch of
-// row t is stored at chunk position ch ^ swz(t). With swz(t) = (2t + t/8) mod 16 (a
-// permutation of 0..15), the 16 lanes writing one chunk of 16 consecutive rows hit 16
-// different bank groups, and the transposed reads (4 rows x 2 chunks per 16 lanes) do too.
-__device__ __forceinline__ int vswz(int row) { return ((row << 1) + ((row >> 3) & 1)) & 15; }
+// row t is stored at chunk position ch ^ swz(t). Measured on gfx950 (LDS bank-conflict
+// counters against two layouts), the 16-byte writes are served 8 lanes (one chunk of 8
+// aligned consecutive rows) per cycle and the transposed 8-byte reads 32 lanes (8 aligned
+// rows x chunks {2j, 2j + 1}) per cycle. swz(t) = (2t + t/4 mod 2) mod 16 takes 8 different
+// values mod 8 on 8 aligned rows, and 8 different values of swz >> 1 mod 8 on them, so
+// neither access conflicts (d = 128; at d = 64 two rows share a 256-byte line).
+__device__ __forceinline__ int vswz(int row) { return ((row << 1) + ((row >> 2) & 1)) & 15; }
 
 // A wave's position in its split's range of sub-chunks. Sub-chunk u is sub-chunk
 // u mod (P/32) of union entry u / (P/32); sub-chunks that no row of the tile can see (past
