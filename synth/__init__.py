@@ -163,7 +163,7 @@ class Config:
     """
     name: str
     batch: int
-    rows: int                    # verify rows per request (1 = plain decode)
+    rows: object                 # rows per request (1 = plain decode): an int, or (lo, hi) drawn per request
     q_heads: int
     kv_heads: int
     head_dim: int
@@ -292,8 +292,17 @@ def generate(cfg, threads: Optional[int] = None) -> Workload:
     root = np.random.SeedSequence(cfg.seed)
     meta_seed, kv_seed = root.spawn(2)
     rng = np.random.Generator(np.random.PCG64(meta_seed))
-    B, R, Hq, Hkv, d, P = cfg.batch, cfg.rows, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.page_size
+    B, Hq, Hkv, d, P = cfg.batch, cfg.q_heads, cfg.kv_heads, cfg.head_dim, cfg.page_size
     assert d % 16 == 0 and Hq % Hkv == 0
+    # rows per request: fixed, or drawn per request from a child seed of its own (so fixed-row
+    # workloads draw exactly what they always did)
+    if isinstance(cfg.rows, (tuple, list)):
+        (rows_seed,) = root.spawn(1)
+        lo_r, hi_r = cfg.rows
+        rows_b = np.random.Generator(np.random.PCG64(rows_seed)).integers(lo_r, hi_r, size=B,
+                                                                          endpoint=True).astype(np.int32)
+    else:
+        rows_b = np.full(B, int(cfg.rows), dtype=np.int32)
 
     # context lengths (include this step's R rows)
     if isinstance(cfg.context, (tuple, list)):
@@ -301,6 +310,7 @@ def generate(cfg, threads: Optional[int] = None) -> Workload:
         seq = rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
     else:
         seq = np.full(B, int(cfg.context), dtype=np.int32)
+    seq = np.maximum(seq, rows_b)                  # a request holds at least its own rows
     n_pages = (seq.astype(np.int64) + P - 1) // P
     MP = int(cfg.max_pages) if cfg.max_pages is not None else int(max(1, n_pages.max(initial=0)))
     assert MP >= n_pages.max(initial=0)
@@ -326,8 +336,8 @@ def generate(cfg, threads: Optional[int] = None) -> Workload:
             if m:
                 page_table[b, rng.choice(n, size=m, replace=False)] = -1
 
-    row_offsets = np.arange(B + 1, dtype=np.int32) * R
-    N = B * R
+    row_offsets = np.concatenate([[0], np.cumsum(rows_b)]).astype(np.int32)
+    N = int(row_offsets[-1])
     q = bf16_bits_from_f32(rng.standard_normal((N, Hq, d), dtype=np.float32))
 
     # K / V pages in physical-page order, one child seed per chunk
@@ -354,7 +364,7 @@ def generate(cfg, threads: Optional[int] = None) -> Workload:
     # copied index keys: groups of candidate pages share one source page's key
     if cfg.dup_key_frac > 0:
         for b in range(B):
-            r_b = R
+            r_b = int(rows_b[b])
             n_min = -(-max(0, int(seq[b]) - r_b + 1) // P)            # pages of the shortest row
             cand = [p for p in range(max(0, n_min - cfg.window)) if page_table[b, p] >= 0]
             m = int(round(cfg.dup_key_frac * len(cand)))

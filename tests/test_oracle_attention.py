@@ -61,7 +61,9 @@ def _dense_reference(w, selected):
     return out, lse
 
 
-@pytest.mark.parametrize("kw", [dict(), dict(invalid_frac=0.2, seed=12), dict(rows=4, context=(40, 130), seed=13)])
+@pytest.mark.parametrize("kw", [dict(), dict(invalid_frac=0.2, seed=12), dict(rows=4, context=(40, 130), seed=13),
+                                dict(rows=24, context=(40, 160), seed=19),                 # a context step
+                                dict(rows=(1, 20), context=(10, 160), seed=20, invalid_frac=0.1)])   # mixed
 def test_attention_matches_dense_bruteforce(kw):
     w = _small(**kw)
     sel = oracle.select_w(w, oracle.index_scores(w))

@@ -33,6 +33,19 @@ def test_rows_closed_form_small():
     assert list(rq) == [0, 0, 0, 0, 1]
 
 
+def test_rows_context_step():
+    """A context step: R rows at the end of L tokens; row j sees L - (R - 1 - j) of them
+    (the causal prefix), in requests of different row counts."""
+    seq = np.array([300, 40, 7], np.int32)
+    ro = np.array([0, 128, 168, 175], np.int32)               # 128, 40 and 7 rows
+    rq, rl, rn = oracle.rows(seq, ro, 64, 8)
+    assert list(rl[:128]) == list(range(300 - 127, 301))
+    assert list(rl[128:168]) == list(range(1, 41))
+    assert list(rl[168:]) == list(range(1, 8))
+    assert list(rn[:128]) == [-(-L // 64) for L in range(173, 301)]
+    assert list(rq) == [0] * 128 + [1] * 40 + [2] * 7
+
+
 def test_rows_configs():
     w = synth.generate("mtp_verify_32k")
     rq, rl, rn = oracle.rows(w.seq_lens, w.row_offsets, 64, w.MP)
