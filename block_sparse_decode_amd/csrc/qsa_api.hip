@@ -12,10 +12,11 @@ using namespace qsa;
 
 namespace {
 
-constexpr int kMaxRows = 4;
+constexpr int kMaxRows = 1024;       // rows per request: decode, MTP verify, context and mixed steps
+constexpr int kStoreMaxRows = 4;     // rows per request the KV store takes
+constexpr int kTileMaxRows = 4;      // rows per attention tile (row-mask byte, union bound)
 constexpr int kMaxPages = 4096;
 constexpr int kMaxKW = 256;
-constexpr int kMaxCols = 64;
 constexpr int kMaxSplits = 64;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -60,7 +61,7 @@ int tile_cols(const qsa_shape *sh)
 {
     const int G = sh->num_q_heads / sh->num_kv_heads;
     if (G >= 16) return 16;
-    int rows = std::max(1, std::min(sh->max_rows_per_request, 16 / G));
+    int rows = std::max(1, std::min({sh->max_rows_per_request, 16 / G, kTileMaxRows}));
     auto tiles = [&](int r) {
         return (int64_t)sh->num_requests * sh->num_kv_heads * ((sh->max_rows_per_request + r - 1) / r);
     };
@@ -198,7 +199,6 @@ qsa_status qsa_select_topk(const qsa_shape *sh, const qsa_paged *pg, const float
 size_t qsa_workspace_bytes(const qsa_shape *sh, int32_t num_splits)
 {
     if (check_shape(sh) != QSA_OK) return 0;
-    if (sh->max_rows_per_request * (sh->num_q_heads / sh->num_kv_heads) > kMaxCols) return 0;
     return decode_ws_bytes(sh, resolve_splits(sh, num_splits));
 }
 
@@ -215,7 +215,6 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     qsa_status st = check_shape(sh);
     if (st != QSA_OK) return st;
     if ((st = check_rows_ptrs(pg)) != QSA_OK) return st;
-    if (sh->max_rows_per_request * (sh->num_q_heads / sh->num_kv_heads) > kMaxCols) return QSA_ERR_UNSUPPORTED;
     if (num_splits < 0) return QSA_ERR_INVALID_ARG;
     if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
     const bool nvfp4 = sh->kv_format == QSA_KV_NVFP4;
@@ -329,7 +328,7 @@ qsa_status qsa_kv_store(const qsa_shape *sh, const qsa_paged *pg, const uint16_t
 {
     qsa_status st = check_shape(sh);
     if (st != QSA_OK) return st;
-    if (sh->kv_format != QSA_KV_NVFP4) return QSA_ERR_UNSUPPORTED;
+    if (sh->kv_format != QSA_KV_NVFP4 || sh->max_rows_per_request > kStoreMaxRows) return QSA_ERR_UNSUPPORTED;
     if ((st = check_rows_ptrs(pg)) != QSA_OK) return st;
     if (sh->num_rows == 0 || sh->num_requests == 0) return QSA_OK;
     if (!new_k || !new_v || !pg->page_table || !pg->k_codes || !pg->k_scales || !pg->v_codes || !pg->v_scales ||

@@ -59,7 +59,9 @@ typedef enum qsa_status {
 typedef struct qsa_shape {
     int32_t num_requests;          /* B >= 0 */
     int32_t num_rows;              /* N = row_offsets[B] >= 0 (the caller knows it) */
-    int32_t max_rows_per_request;  /* 1..4: upper bound on row_offsets[b+1] - row_offsets[b] */
+    int32_t max_rows_per_request;  /* 1..1024: upper bound on row_offsets[b+1] - row_offsets[b]
+                                      (1 decode, 2..4 MTP verify, more: a context or mixed step;
+                                      qsa_kv_store takes 1..4) */
     int32_t num_q_heads;           /* Hq >= 1, a multiple of Hkv */
     int32_t num_kv_heads;          /* Hkv >= 1 */
     int32_t head_dim;              /* d: 64 or 128 */

@@ -95,7 +95,7 @@ def _rawd(name, *args):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), 2), (dict(head_dim=256), 2), (dict(page_size=32), 2), (dict(max_pages=4097), 2),
-    (dict(topk=250, window=7), 2), (dict(max_rows_per_request=5), 2),
+    (dict(topk=250, window=7), 2), (dict(max_rows_per_request=1025), 2),
     (dict(num_q_heads=30), 1), (dict(num_kv_heads=0), 1), (dict(num_requests=-1), 1), (dict(topk=-1), 1),
     (dict(max_pages=0), 1), (dict(num_rows=9), 1), (dict(sm_scale=float("inf")), 1),
 ])
@@ -134,10 +134,9 @@ def test_pointer_validation():
                     FAKE, 1 << 30, None) == 1
         assert _rawd("qsa_select_sparse_decode", ctypes.byref(bad_sh), ctypes.byref(bad_pg), FAKE, FAKE, FAKE,
                     FAKE, None, 0, FAKE, 1 << 30, None) == 1
-    # too many q columns per request (4 rows x 32 heads per KV head)
-    big = _shape(num_q_heads=128)
-    assert _rawd("qsa_sparse_decode", ctypes.byref(big), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 0, FAKE,
-                1 << 30, None) == 2
+    # the KV store takes at most 4 rows per request (a context step's rows are stored elsewhere)
+    assert _raw("qsa_kv_store", ctypes.byref(_shape(max_rows_per_request=16, num_rows=16)), ctypes.byref(pg), FAKE,
+                FAKE, None) == 2
 
 
 def test_kv_format_and_gate_validation():
