@@ -177,6 +177,22 @@ def store_bytes(w):
     return new_in + new_out + old_k + keys
 
 
+def attention_flop(w, selected):
+    """MFMA work the attention must do: 4 d flop (q.k and p.v) per (row, q head, visible
+    selected token)."""
+    c = w.cfg
+    P = c.page_size
+    toks = 0
+    for b in range(w.B):
+        r0, r1 = int(w.row_offsets[b]), int(w.row_offsets[b + 1])
+        for j in range(r1 - r0):
+            L = int(w.seq_lens[b]) - (r1 - r0 - 1 - j)
+            for p in set(int(x) for x in selected[r0 + j] if x >= 0):
+                if w.page_table[b, p] >= 0:
+                    toks += max(0, min(P, L - p * P))
+    return 4 * c.head_dim * c.q_heads * toks
+
+
 def fused_kernel_name(w):
     """Name rocprofv3 gives the fused selection + attention kernel for this workload."""
     c = w.cfg
@@ -372,6 +388,34 @@ def main():
         return a.elapsed_time(b2) * 1e3 / K
     fp8_us = stage8_us(lambda st: st.select_decode_call(stream))
     fp8_bytes = algorithmic_bytes(w8, sel8)["select_attention"]
+    del steps8, layers8, base8, b8
+
+    # (6) a context step: 4 requests x 256 causal rows of 8K tokens (16 layer copies, 290 MB)
+    wc = synth.generate("context_8k")
+    basec = DeviceBatch.upload(wc, dev)
+    layersc = [basec]
+    for _ in range(15):
+        bc = DeviceBatch(**{**basec.__dict__})
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "index_keys"):
+            setattr(bc, name, getattr(basec, name).clone())
+        layersc.append(bc)
+    stepsc = [Step(b, num_splits=args.splits) for b in layersc]
+    for st in stepsc:
+        st(stream)
+    torch.cuda.synchronize()
+    selc = stepsc[0].selected.cpu().numpy()
+
+    def stagec_us(fn):
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(K):
+            fn(stepsc[i % len(stepsc)])
+        b2.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b2) * 1e3 / K
+    ctx_index_us = stagec_us(lambda st: st.scores_call(stream))
+    ctx_attn_us = stagec_us(lambda st: st.select_decode_call(stream))
+    ctx_flop = attention_flop(wc, selc)
     err = int(base.error_word[0].item())
 
     ab = algorithmic_bytes(w, sel)
@@ -410,6 +454,9 @@ def main():
                    "gated_select_sparse_decode_us": round(gated_us, 2),
                    "fp8_select_sparse_decode_us": round(fp8_us, 2),
                    "fp8_select_attention_gbs": round(fp8_bytes / (fp8_us * 1e-6) / 1e9, 1),
+                   "context_8k_index_scores_us": round(ctx_index_us, 2),
+                   "context_8k_select_sparse_decode_us": round(ctx_attn_us, 2),
+                   "context_8k_attention_tflops": round(ctx_flop / (ctx_attn_us * 1e-6) / 1e12, 1),
                    "timing": "mean of back-to-back launches between one HIP event pair on the launch stream"},
         "bytes": ab,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

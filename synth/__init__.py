@@ -198,6 +198,9 @@ CONFIGS = {
     # 4 rows, 64/8 heads, 131K context in 128-token pages, 1% +-8.0 outliers.
     "long_131k": Config("long_131k", 4, 1, 64, 8, 128, 128, 131072, 64, 1, seed=3,
                         outlier_frac=0.01),
+    # a context step: 4 requests x 256 causal rows (the last 256 of 8K tokens), 32/4 heads,
+    # d 128, each row selecting k 32 + W 2 of its pages.
+    "context_8k": Config("context_8k", 4, 256, 32, 4, 128, 64, 8192, 32, 2, seed=5),
     # 48 requests x 4 rows, context U[1024, 65536], 5% invalid page-table entries.
     "wide_mixed": Config("wide_mixed", 48, 4, 32, 4, 128, 64, (1024, 65536), 32, 2, seed=4,
                          invalid_frac=0.05),
