@@ -275,26 +275,26 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     // ---- 1. union of the tile's rows' selected pages; the q operand ------------------
     // All threads stage this request's page-table row in LDS (scratch in the V staging
     // area, with a row-mask bitmap of one byte per page and an owner word per page) while
-    // wave 0 loads the tile's selection rows and wave 1 loads q, so the union costs one
-    // dependent global round trip. Then wave 0 alone builds the union: each listed page
-    // ORs its row into the bitmap and bids its entry index for the page's owner word (the
-    // smallest bid wins), and each page's owner appends it, with ballot counts for the
-    // positions, so no workgroup barrier is needed. Meanwhile wave 1 converts q into the
-    // MFMA B operand in LDS. Union order: by first listing (rows in order), a function
-    // of the input alone.
+    // the selecting waves load their score rows (or wave 0 the selection rows) and the last
+    // wave loads q, so the union costs one dependent global round trip. Then wave 0 alone
+    // builds the union: each listed page ORs its row into the bitmap and bids its entry
+    // index for the page's owner word (the smallest bid wins), and each page's owner
+    // appends it, with ballot counts for the positions, so no workgroup barrier is needed.
+    // Meanwhile the last wave converts q into the MFMA B operand in LDS. Union order: by
+    // first listing (rows in order), a function of the input alone.
     const int nwords = ((MP + 3) / 4 + 3) & ~3;
     uint32_t *bm = reinterpret_cast<uint32_t *>(lds_area);
     int32_t *pt_row = reinterpret_cast<int32_t *>(bm + nwords);
     uint32_t *owner = reinterpret_cast<uint32_t *>(pt_row + MP);
-    for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
-    for (int p = tid; p < MP; p += NT) {
-        pt_row[p] = prm.page_table[(int64_t)b * MP + p];
-        owner[p] = 0xffffffffu;
-    }
     const int nent = nrow * KW;                      // <= kMaxUnion
     constexpr int kSelPerLane = kMaxUnion / 64;
     int selp[kSelPerLane];
     int32_t *sel_lds = reinterpret_cast<int32_t *>(u_pm);   // the selections, before the union
+
+    // The independent global loads go first, so that no wave waits for one of them before
+    // issuing the next: each selecting wave's score row (or wave 0's selection rows), the
+    // last wave's q columns, then every thread's page-table entries (whose LDS stores wait).
+    uint32_t skey[SELC > 0 ? SELC : 8];
     if constexpr (SELC == 0) {
 #pragma unroll
         for (int i = 0; i < kSelPerLane; ++i) {
@@ -306,12 +306,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
             }
         }
     } else {
-        // wave w selects the tile's row j_lo + w, into LDS
-        if (wave < nrow) {
-            const int jw = j_lo + wave;
-            select_row<SELC, false>(prm.scores + (int64_t)(r0 + jw) * MP, MP, row_geom(Lb, Rb, jw, prm.log2P, MP).pages,
-                                    prm.k, prm.W, sel_lds + wave * KW);
-        }
+        if (wave < nrow) select_row_load<SELC, false>(prm.scores + (int64_t)(r0 + j_lo + wave) * MP, MP, skey);
     }
     // this lane's query column
     const int col = col0 + li;
@@ -325,6 +320,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         const uint4 *qp = reinterpret_cast<const uint4 *>(prm.q + ((int64_t)(r0 + jc) * prm.Hq + h) * D + gq * DQ);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qraw[ks] = qp[ks];
+    }
+    for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
+    for (int p = tid; p < MP; p += NT) {
+        pt_row[p] = prm.page_table[(int64_t)b * MP + p];
+        owner[p] = 0xffffffffu;
+    }
+    if constexpr (SELC > 0) {
+        // wave w selects the tile's row j_lo + w, into LDS
+        if (wave < nrow)
+            select_row_keys<SELC>(skey, row_geom(Lb, Rb, j_lo + wave, prm.log2P, MP).pages, prm.k, prm.W,
+                                  sel_lds + wave * KW);
     }
     __syncthreads();
     if (wave == 0) {

@@ -41,19 +41,14 @@ __device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[C], uint
     return c;
 }
 
-// srow: the row's MP scores; n: the row's visible pages; dst: the row's k + W output slots.
+// The row's scores as raw bits, lane l holding columns l*C .. l*C + C - 1 (0 past MP).
+// Split from the selection itself so that a caller can issue these loads early.
 // COHERENT: the scores were written by other workgroups of the same launch, so they are
 // read with agent-scope loads.
 template <int C, bool COHERENT>
-__device__ __forceinline__ void select_row(const float *srow, int MP, int n, int k_, int W, int32_t *dst)
+__device__ __forceinline__ void select_row_load(const float *srow, int MP, uint32_t (&key)[C])
 {
-    const int lane = threadIdx.x & 63;
-    const int KW = k_ + W;
-    const int wlo = n - W > 0 ? n - W : 0;
-    const int c0 = lane * C;
-
-    // 1. keys; 0 marks a non-candidate
-    uint32_t key[C];
+    const int c0 = (threadIdx.x & 63) * C;
     if constexpr (COHERENT) {
 #pragma unroll
         for (int i = 0; i < C; ++i)
@@ -71,6 +66,19 @@ __device__ __forceinline__ void select_row(const float *srow, int MP, int n, int
 #pragma unroll
         for (int i = 0; i < C; ++i) key[i] = c0 + i < MP ? __float_as_uint(srow[c0 + i]) : 0u;
     }
+}
+
+// The selection from the loaded score bits. n: the row's visible pages; dst: the row's
+// k + W output slots.
+template <int C>
+__device__ __forceinline__ void select_row_keys(uint32_t (&key)[C], int n, int k_, int W, int32_t *dst)
+{
+    const int lane = threadIdx.x & 63;
+    const int KW = k_ + W;
+    const int wlo = n - W > 0 ? n - W : 0;
+    const int c0 = lane * C;
+
+    // 1. keys; 0 marks a non-candidate
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int p = c0 + i;
@@ -130,6 +138,15 @@ __device__ __forceinline__ void select_row(const float *srow, int MP, int n, int
         }
     }
     for (int i = (int)total + lane; i < KW; i += 64) dst[i] = -1;
+}
+
+// srow: the row's MP scores; n: the row's visible pages; dst: the row's k + W output slots.
+template <int C, bool COHERENT>
+__device__ __forceinline__ void select_row(const float *srow, int MP, int n, int k_, int W, int32_t *dst)
+{
+    uint32_t key[C];
+    select_row_load<C, COHERENT>(srow, MP, key);
+    select_row_keys<C>(key, n, k_, W, dst);
 }
 
 }  // namespace qsa
