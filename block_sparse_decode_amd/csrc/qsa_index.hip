@@ -59,66 +59,89 @@ __global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(Index
     const int G = prm.Hq / prm.Hkv;
     float(*qw)[HG] = qs[wv];
     float best = __builtin_nanf("");
-    for (int g = wv; g < prm.Hkv && any_cand; g += NW) {
-        // this page's key for KV head g, as fp32 in registers
-        float k[D];
-        {
-            const uint4 *kp = reinterpret_cast<const uint4 *>(prm.keys + ((int64_t)(cand ? phys : 0) * prm.Hkv + g) * D);
+    // q heads h0 .. h0 + nh - 1 of KV head g, as bf16 pairs: lane l holds elements 2l, 2l + 1
+    // of every head (zeros past nh, and for lanes past d / 2)
+    auto load_q = [&](int g, int h0, uint32_t (&qu)[HG]) {
+        const int nh = min(HG, G - h0);
+        const uint32_t *qb = prm.q32 + ((int64_t)row * prm.Hq + g * G + h0) * (D / 2) + lane;
 #pragma unroll
-            for (int c = 0; c < D / 8; ++c) {
-                const uint4 v = kp[c];
-                k[8 * c + 0] = bf16lo(v.x); k[8 * c + 1] = bf16hi(v.x);
-                k[8 * c + 2] = bf16lo(v.y); k[8 * c + 3] = bf16hi(v.y);
-                k[8 * c + 4] = bf16lo(v.z); k[8 * c + 5] = bf16hi(v.z);
-                k[8 * c + 6] = bf16lo(v.w); k[8 * c + 7] = bf16hi(v.w);
-            }
+        for (int t = 0; t < HG; ++t) qu[t] = (lane < D / 2 && t < nh) ? qb[t * (D / 2)] : 0u;
+    };
+    auto stage_q = [&](const uint32_t (&qu)[HG]) {
+        if (lane < D / 2) {
+            float4 *d0 = reinterpret_cast<float4 *>(qw[2 * lane]);
+            float4 *d1 = reinterpret_cast<float4 *>(qw[2 * lane + 1]);
+            d0[0] = make_float4(bf16lo(qu[0]), bf16lo(qu[1]), bf16lo(qu[2]), bf16lo(qu[3]));
+            d0[1] = make_float4(bf16lo(qu[4]), bf16lo(qu[5]), bf16lo(qu[6]), bf16lo(qu[7]));
+            d1[0] = make_float4(bf16hi(qu[0]), bf16hi(qu[1]), bf16hi(qu[2]), bf16hi(qu[3]));
+            d1[1] = make_float4(bf16hi(qu[4]), bf16hi(qu[5]), bf16hi(qu[6]), bf16hi(qu[7]));
         }
-        for (int h0 = 0; h0 < G; h0 += HG) {
-            const int nh = min(HG, G - h0);
-            // stage q heads h0 .. h0 + nh - 1 of KV head g: lane l writes elements 2l, 2l + 1
-            // of every head (zeros past nh)
-            if (lane < D / 2) {
-                const uint32_t *qb = prm.q32 + ((int64_t)row * prm.Hq + g * G + h0) * (D / 2) + lane;
-                float lo[HG], hi[HG];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): this wave's q rows are in LDS
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    // the eight chains over elements i0 .. i0 + 7, each in ascending element order
+    auto chains8 = [&](const float (&k)[D], int i0, float (&a)[HG]) {
 #pragma unroll
-                for (int t = 0; t < HG; ++t) {
-                    const uint32_t u = t < nh ? qb[t * (D / 2)] : 0u;
-                    lo[t] = bf16lo(u);
-                    hi[t] = bf16hi(u);
-                }
-                float4 *d0 = reinterpret_cast<float4 *>(qw[2 * lane]);
-                float4 *d1 = reinterpret_cast<float4 *>(qw[2 * lane + 1]);
-                d0[0] = make_float4(lo[0], lo[1], lo[2], lo[3]);
-                d0[1] = make_float4(lo[4], lo[5], lo[6], lo[7]);
-                d1[0] = make_float4(hi[0], hi[1], hi[2], hi[3]);
-                d1[1] = make_float4(hi[4], hi[5], hi[6], hi[7]);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): this wave's q rows are in LDS
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // eight chains, one per head, each in ascending element order
-            float a[HG];
+        for (int i = i0; i < i0 + 8; ++i) {
+            const float4 qa = *reinterpret_cast<const float4 *>(&qw[i][0]);
+            const float4 qb2 = *reinterpret_cast<const float4 *>(&qw[i][4]);
+            a[0] = __builtin_fmaf(qa.x, k[i], a[0]);
+            a[1] = __builtin_fmaf(qa.y, k[i], a[1]);
+            a[2] = __builtin_fmaf(qa.z, k[i], a[2]);
+            a[3] = __builtin_fmaf(qa.w, k[i], a[3]);
+            a[4] = __builtin_fmaf(qb2.x, k[i], a[4]);
+            a[5] = __builtin_fmaf(qb2.y, k[i], a[5]);
+            a[6] = __builtin_fmaf(qb2.z, k[i], a[6]);
+            a[7] = __builtin_fmaf(qb2.w, k[i], a[7]);
+        }
+    };
+    auto fold = [&](const float (&a)[HG], int nh) {
+#pragma unroll
+        for (int t = 0; t < HG; ++t)
+            if (t < nh && !(a[t] != a[t]) && ((best != best) || a[t] > best)) best = a[t];
+    };
+
+    for (int g = wv; g < prm.Hkv && any_cand; g += NW) {
+        // q of the first head group, then this page's key for KV head g: every load is issued
+        // before the first wait, and the q loads first, so waiting for q leaves the key loads
+        // in flight (the memory counter is in order)
+        uint32_t qu[HG];
+        load_q(g, 0, qu);
+        const uint4 *kp = reinterpret_cast<const uint4 *>(prm.keys + ((int64_t)(cand ? phys : 0) * prm.Hkv + g) * D);
+        uint4 kraw[D / 8];
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) kraw[c] = kp[c];
+        __builtin_amdgcn_sched_barrier(0);    // keep every key load ahead of the wait for q
+        stage_q(qu);
+        // first head group: each 8-element chunk of the key is converted to fp32 and used as
+        // soon as it has arrived, while the later chunks are still in flight
+        float k[D];
+        float a[HG];
+#pragma unroll
+        for (int t = 0; t < HG; ++t) a[t] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const uint4 v = kraw[c];
+            k[8 * c + 0] = bf16lo(v.x); k[8 * c + 1] = bf16hi(v.x);
+            k[8 * c + 2] = bf16lo(v.y); k[8 * c + 3] = bf16hi(v.y);
+            k[8 * c + 4] = bf16lo(v.z); k[8 * c + 5] = bf16hi(v.z);
+            k[8 * c + 6] = bf16lo(v.w); k[8 * c + 7] = bf16hi(v.w);
+            chains8(k, 8 * c, a);
+        }
+        fold(a, min(HG, G));
+        // further head groups reuse the converted key
+        for (int h0 = HG; h0 < G; h0 += HG) {
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's reads of the previous group are done
+            load_q(g, h0, qu);
+            stage_q(qu);
 #pragma unroll
             for (int t = 0; t < HG; ++t) a[t] = 0.0f;
 #pragma unroll
-            for (int i = 0; i < D; ++i) {
-                const float4 qa = *reinterpret_cast<const float4 *>(&qw[i][0]);
-                const float4 qb2 = *reinterpret_cast<const float4 *>(&qw[i][4]);
-                a[0] = __builtin_fmaf(qa.x, k[i], a[0]);
-                a[1] = __builtin_fmaf(qa.y, k[i], a[1]);
-                a[2] = __builtin_fmaf(qa.z, k[i], a[2]);
-                a[3] = __builtin_fmaf(qa.w, k[i], a[3]);
-                a[4] = __builtin_fmaf(qb2.x, k[i], a[4]);
-                a[5] = __builtin_fmaf(qb2.y, k[i], a[5]);
-                a[6] = __builtin_fmaf(qb2.z, k[i], a[6]);
-                a[7] = __builtin_fmaf(qb2.w, k[i], a[7]);
-            }
-#pragma unroll
-            for (int t = 0; t < HG; ++t)
-                if (t < nh && !(a[t] != a[t]) && ((best != best) || a[t] > best)) best = a[t];
-            // the next group's staging overwrites qw: this wave's reads are complete
-            __builtin_amdgcn_s_waitcnt(0xc07f);
+            for (int c = 0; c < D / 8; ++c) chains8(k, 8 * c, a);
+            fold(a, min(HG, G - h0));
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // reads done before the next KV head's staging
     }
     red[wave][lane] = best;
     __syncthreads();
