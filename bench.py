@@ -224,6 +224,40 @@ def cpu_baseline(w, max_rows):
     return per_step_s, rows, dt
 
 
+def context_stage(args, q, synth, DeviceBatch, Step, dev, stream, K):
+    """Index scores and the fused attention of a context step (4 requests x 256 causal rows
+    of 8K tokens, 16 layer copies of the pools), each timed over K back-to-back launches."""
+    import torch
+    wc = synth.generate("context_8k")
+    basec = DeviceBatch.upload(wc, dev)
+    layersc = [basec]
+    for _ in range(15):
+        bc = DeviceBatch(**{**basec.__dict__})
+        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "index_keys"):
+            setattr(bc, name, getattr(basec, name).clone())
+        layersc.append(bc)
+    stepsc = [Step(b, num_splits=args.splits) for b in layersc]
+    for st in stepsc:
+        st(stream)
+    torch.cuda.synchronize()
+    selc = stepsc[0].selected.cpu().numpy()
+
+    def stagec_us(fn):
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(K):
+            fn(stepsc[i % len(stepsc)])
+        b2.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b2) * 1e3 / K
+    ctx_index_us = stagec_us(lambda st: st.scores_call(stream))
+    ctx_attn_us = stagec_us(lambda st: st.select_decode_call(stream))
+    ctx_flop = attention_flop(wc, selc)
+    return {"context_8k_index_scores_us": round(ctx_index_us, 2),
+            "context_8k_select_sparse_decode_us": round(ctx_attn_us, 2),
+            "context_8k_attention_tflops": round(ctx_flop / (ctx_attn_us * 1e-6) / 1e12, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +267,9 @@ def main():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=48, help="rows of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--context", action="store_true",
+                    help="also time a context step (4 x 256 rows of 8K; its attention launches the same kernel as "
+                         "the verify step, so it is off when profiling that kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for PMC byte-counter scaling)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -390,32 +427,11 @@ def main():
     fp8_bytes = algorithmic_bytes(w8, sel8)["select_attention"]
     del steps8, layers8, base8, b8
 
-    # (6) a context step: 4 requests x 256 causal rows of 8K tokens (16 layer copies, 290 MB)
-    wc = synth.generate("context_8k")
-    basec = DeviceBatch.upload(wc, dev)
-    layersc = [basec]
-    for _ in range(15):
-        bc = DeviceBatch(**{**basec.__dict__})
-        for name in ("k_codes", "k_scales", "v_codes", "v_scales", "index_keys"):
-            setattr(bc, name, getattr(basec, name).clone())
-        layersc.append(bc)
-    stepsc = [Step(b, num_splits=args.splits) for b in layersc]
-    for st in stepsc:
-        st(stream)
-    torch.cuda.synchronize()
-    selc = stepsc[0].selected.cpu().numpy()
+    # (6) a context step (--context): 4 requests x 256 causal rows of 8K tokens
+    ctx_stages = {}
+    if args.context:
+        ctx_stages = context_stage(args, q, synth, DeviceBatch, Step, dev, stream, K)
 
-    def stagec_us(fn):
-        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(K):
-            fn(stepsc[i % len(stepsc)])
-        b2.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b2) * 1e3 / K
-    ctx_index_us = stagec_us(lambda st: st.scores_call(stream))
-    ctx_attn_us = stagec_us(lambda st: st.select_decode_call(stream))
-    ctx_flop = attention_flop(wc, selc)
     err = int(base.error_word[0].item())
 
     ab = algorithmic_bytes(w, sel)
@@ -454,9 +470,7 @@ def main():
                    "gated_select_sparse_decode_us": round(gated_us, 2),
                    "fp8_select_sparse_decode_us": round(fp8_us, 2),
                    "fp8_select_attention_gbs": round(fp8_bytes / (fp8_us * 1e-6) / 1e9, 1),
-                   "context_8k_index_scores_us": round(ctx_index_us, 2),
-                   "context_8k_select_sparse_decode_us": round(ctx_attn_us, 2),
-                   "context_8k_attention_tflops": round(ctx_flop / (ctx_attn_us * 1e-6) / 1e12, 1),
+                   **ctx_stages,
                    "timing": "mean of back-to-back launches between one HIP event pair on the launch stream"},
         "bytes": ab,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
