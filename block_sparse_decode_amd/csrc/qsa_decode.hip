@@ -1,16 +1,19 @@
-// qsa_decode.hip -- split-KV sparse GQA attention over NVFP4 pages, with LSE merge.
+// qsa_decode.hip -- split-KV sparse GQA attention over NVFP4 (or FP8) pages, with LSE merge.
 //
 // Method: TensorRT-LLM PR #20937, Description > What changes: NVFP4 sparse GQA decode as a
-// split-K + merge kernel with a lean one-split variant, and a request-grouped verify kernel
-// with a per-row merge. PR #20276, "What runs on the fast paths": K/V tiles are read once
-// per group of rows of one request.
+// split-K + merge kernel with a lean one-split variant, a request-grouped verify kernel with
+// a per-row merge and a gated epilogue, and a row-tile pass for context and mixed steps.
+// PR #20276, "What runs on the fast paths": K/V tiles are read once per group of rows of one
+// request.
 //
 // Work item: a tile is (request b, KV head g, a run of at most 16 of the request's R x G
 // query columns, whole rows when G <= 16); each tile is split S ways, one 8-wave workgroup
 // per (tile, split). The host picks the rows per tile and S (see tile_cols and auto_splits
 // in qsa_api.hip): rows are grouped only while that still leaves a tile per CU, since
 // splitting a tile's pages instead costs a merge.
-//  1. The tile's rows (up to 4 causal verify rows) each list their selected pages. Wave 0
+//  1. The tile's rows (at most 4 causal rows: verify rows, or a run of a context step's
+//     rows) each list their selected pages (computed here from the scores, one wave per
+//     row, when the selection is fused in). Wave 0
 //     builds the union of those pages, each with a row bitmask, in LDS, and drops entries
 //     whose page-table entry is -1. Each page of the union is read once for all the
 //     tile's rows.
@@ -32,7 +35,8 @@
 // split) map gives each XCD a contiguous run of (request, KV head, column tile, split)
 // items, so a tile's splits, and the tiles of one request and KV head (whose rows share
 // their window pages and often more), run on one XCD and share its L2.
-// NVFP4 -> f16 is exact (see nvfp4_dequant8). The global scales fold into the logit scale
+// NVFP4 -> f16 and E4M3 -> f16 are exact (see nvfp4_dequant8, fp8x8_to_f16x8). With a gate the
+// output is o * sigmoid(gate) before its one bf16 rounding. The global scales fold into the logit scale
 // and the output.
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"

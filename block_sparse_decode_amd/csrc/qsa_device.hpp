@@ -24,7 +24,6 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
@@ -109,18 +108,11 @@ __device__ __forceinline__ int clip_rows(int r0, int r1, int N, int rmax, uint32
     return R;
 }
 
-// Wave-wide reductions over the lanes that share a 16-lane column slot (xor 16, xor 32).
+// Wave-wide max over the lanes that share a 16-lane column slot (xor 16, xor 32).
 __device__ __forceinline__ float max_across_groups(float v)
 {
     v = fmaxf(v, __shfl_xor(v, 16, 64));
     v = fmaxf(v, __shfl_xor(v, 32, 64));
-    return v;
-}
-
-__device__ __forceinline__ float sum_across_groups(float v)
-{
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
     return v;
 }
 

@@ -3,7 +3,7 @@
 // Method: TensorRT-LLM PR #20276, Features, "Canonical QSA selection" (the selection row is a
 // pure function of the scores, the window and k: every block strictly above the k-th score,
 // ties to the highest index) and Decisions worth knowing (the result must not follow launch
-// order). Shared by the select kernel and the fused index + select kernel.
+// order). Shared by the select kernel and the attention kernel's fused selection.
 //
 // One wave, no LDS, no barrier. Lane l holds columns l*C .. l*C + C - 1 (C >= MP/64) as
 // order-preserving uint32 keys in registers, so lane-major order is ascending page order.
