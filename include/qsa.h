@@ -2,19 +2,24 @@
  * qsa.h -- C ABI of the query-sparse NVFP4 decode / verify attention library (libqsa.so).
  *
  * The method (TensorRT-LLM PR #20276, "What runs on the fast paths"; PR #20937,
- * Description > What changes) runs one attention layer of a decode or MTP-verify step
- * over a paged KV cache in three calls:
+ * Description > What changes) runs one attention layer of a decode, MTP-verify, context or
+ * mixed step over a paged KV cache in three calls:
  *
  *   1. qsa_index_scores  -- score every page of every query row against its index key;
  *   2. qsa_select_topk   -- canonical top-k pages plus a local window per row;
  *   3. qsa_sparse_decode -- split-KV softmax attention over the selected pages, with an
- *                           LSE merge of the splits.
+ *                           LSE merge of the splits (optionally gated);
+ *
+ * or in two, with qsa_select_sparse_decode doing 2 and 3 in one launch. Around the step:
+ * qsa_kv_store writes the step's new tokens into the cache and the touched pages' index
+ * keys; qsa_rollback_gather / qsa_rollback_restore save and restore the plane rows of
+ * rejected draft rows (qsa_step_slots gives each row's page and slot).
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers owned by the caller. The library never
  *     allocates, frees or reads device memory from the host, and it never synchronises.
  *     Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream).
- *   - Pointers must be aligned to 16 bytes.
+ *   - Tensor pointers must be aligned to 16 bytes unless a call states otherwise.
  *   - Host-checkable argument errors return a status before any launch. Nothing is
  *     written then. The library never aborts or throws.
  *   - The library keeps no mutable global state. Calls on different streams may run
