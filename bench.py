@@ -427,6 +427,20 @@ def main():
     fp8_bytes = algorithmic_bytes(w8, sel8)["select_attention"]
     del steps8, layers8, base8, b8
 
+    # (7) the reference the measurement is read against: a plain 512 MiB device-to-device copy
+    csrc = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    ca, cb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ca.record(stream)
+    for _ in range(20):
+        cdst.copy_(csrc)
+    cb.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc.numel() / (ca.elapsed_time(cb) * 1e-3 / 20) / 1e9
+    del csrc, cdst
+
     # (6) a context step (--context): 4 requests x 256 causal rows of 8K tokens
     ctx_stages = {}
     if args.context:
@@ -473,6 +487,7 @@ def main():
                    **ctx_stages,
                    "timing": "mean of back-to-back launches between one HIP event pair on the launch stream"},
         "bytes": ab,
+        "reference_copy_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(c.name),
                      "kernel": "qsa_select_sparse_decode (" + fused_kernel_name(w) + ")"},
