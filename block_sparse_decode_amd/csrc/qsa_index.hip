@@ -9,20 +9,46 @@
 // arithmetic must be reproducible bit for bit. It therefore runs on the plain ALUs, never
 // on MFMA, whose internal summation order is not specified. A workgroup covers 64 pages of
 // one query row; each lane owns one page and keeps that page's key for the current KV head
-// in VGPRs as fp32. Each wave takes KV heads in turn. The q heads of a KV head are staged
-// per wave in LDS as fp32, eight heads per element, so one broadcast read (all lanes at one
-// address) feeds eight fma chains, one per head, each still one fp32 fma after another in
-// ascending element order. A product of two bf16 values is exact in fp32, so the fma equals
-// the separate multiply and add. The loads that do not depend on each other (row offsets,
-// the request's length, the page-table entries, q) are issued together at the start. An
-// LDS max over the waves combines the KV heads (max is exact in any order).
+// in VGPRs as fp32. Each wave takes KV heads in turn, eight of the KV head's q heads per
+// pass. q is wave-uniform, so it reaches the lanes through the cross-lane operand network
+// rather than through per-element LDS reads: a VGPR holds 16 consecutive elements of one
+// head, element m in lane m of every 16-lane row, and each v_fmac_f32 reads its q operand
+// through DPP row_newbcast, which hands one lane's value to its whole row. Each head's sum
+// stays one fp32 fma after another in ascending element order. A product of two bf16 values
+// is exact in fp32, so the fma equals the separate multiply and add. The loads that do not
+// depend on each other (row offsets, the request's length, the page-table entries, q) are
+// issued together at the start. An LDS max over the waves combines the KV heads (max is
+// exact in any order).
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
 namespace qsa {
 
 constexpr int kIndexWaves = 4;
-constexpr int kHeadGroup = 8;        // q heads per pass: one LDS row of 8 fp32 per element
+constexpr int kHeadGroup = 8;        // q heads per pass
+
+// acc[t] = fma(q_t[16c + n], k[16c + n], acc[t]) for n = 0 .. 15 in order and t = 0 .. 7:
+// operand 8 + t holds q_t[16c + m] in lane m of each 16-lane row, and row_newbcast:n gives
+// every lane of the row lane n's value. Operands 16 .. 31 are k[16c .. 16c + 15]. The
+// leading s_nop covers the wait states that a DPP read needs after a VALU write of its
+// source or an SALU write of EXEC, which the compiler does not track inside inline asm.
+#define QSA_FMAC(A, Q, K, N) "v_fmac_f32_dpp %" #A ", %" #Q ", %" #K " row_newbcast:" #N " row_mask:0xf bank_mask:0xf\n"
+#define QSA_FMAC8(K, N)                                                                                           \
+    QSA_FMAC(0, 8, K, N) QSA_FMAC(1, 9, K, N) QSA_FMAC(2, 10, K, N) QSA_FMAC(3, 11, K, N) QSA_FMAC(4, 12, K, N) \
+        QSA_FMAC(5, 13, K, N) QSA_FMAC(6, 14, K, N) QSA_FMAC(7, 15, K, N)
+
+__device__ __forceinline__ void fmac16x8(float (&a)[kHeadGroup], const float (&qc)[kHeadGroup], const float *k)
+{
+    asm("s_nop 4\n" QSA_FMAC8(16, 0) QSA_FMAC8(17, 1) QSA_FMAC8(18, 2) QSA_FMAC8(19, 3) QSA_FMAC8(20, 4)
+            QSA_FMAC8(21, 5) QSA_FMAC8(22, 6) QSA_FMAC8(23, 7) QSA_FMAC8(24, 8) QSA_FMAC8(25, 9) QSA_FMAC8(26, 10)
+                QSA_FMAC8(27, 11) QSA_FMAC8(28, 12) QSA_FMAC8(29, 13) QSA_FMAC8(30, 14) QSA_FMAC8(31, 15)
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]), "+v"(a[6]), "+v"(a[7])
+        : "v"(qc[0]), "v"(qc[1]), "v"(qc[2]), "v"(qc[3]), "v"(qc[4]), "v"(qc[5]), "v"(qc[6]), "v"(qc[7]), "v"(k[0]),
+          "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]), "v"(k[7]), "v"(k[8]), "v"(k[9]),
+          "v"(k[10]), "v"(k[11]), "v"(k[12]), "v"(k[13]), "v"(k[14]), "v"(k[15]));
+}
+#undef QSA_FMAC8
+#undef QSA_FMAC
 
 template <int D>
 __global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(IndexParams prm)
@@ -30,7 +56,9 @@ __global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(Index
     constexpr int NW = kIndexWaves;
     constexpr int HG = kHeadGroup;
     __shared__ float red[NW][kWave];
-    __shared__ __align__(16) float qs[NW][D][HG];   // per wave: q[head][i] of one head group, element-major
+    constexpr int NC = D / 16;                        // 16-element chunks of a row
+    // per wave: q of one head group, [head][element mod 16][element / 16]
+    __shared__ __align__(16) float qs[NW][HG][16][NC];
 
     const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -57,7 +85,7 @@ __global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(Index
     const bool any_cand = __any(cand);
 
     const int G = prm.Hq / prm.Hkv;
-    float(*qw)[HG] = qs[wv];
+    float(*qw)[16][NC] = qs[wv];
     float best = __builtin_nanf("");
     // q heads h0 .. h0 + nh - 1 of KV head g, as bf16 pairs: lane l holds elements 2l, 2l + 1
     // of every head (zeros past nh, and for lanes past d / 2)
@@ -67,34 +95,30 @@ __global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(Index
 #pragma unroll
         for (int t = 0; t < HG; ++t) qu[t] = (lane < D / 2 && t < nh) ? qb[t * (D / 2)] : 0u;
     };
-    auto stage_q = [&](const uint32_t (&qu)[HG]) {
+    // q of the head group into LDS as fp32, then into qc[c][t] (head t, elements 16c .. 16c + 15,
+    // element 16c + m in lane m of each 16-lane row)
+    auto stage_q = [&](const uint32_t (&qu)[HG], float (&qc)[NC][HG]) {
         if (lane < D / 2) {
-            float4 *d0 = reinterpret_cast<float4 *>(qw[2 * lane]);
-            float4 *d1 = reinterpret_cast<float4 *>(qw[2 * lane + 1]);
-            d0[0] = make_float4(bf16lo(qu[0]), bf16lo(qu[1]), bf16lo(qu[2]), bf16lo(qu[3]));
-            d0[1] = make_float4(bf16lo(qu[4]), bf16lo(qu[5]), bf16lo(qu[6]), bf16lo(qu[7]));
-            d1[0] = make_float4(bf16hi(qu[0]), bf16hi(qu[1]), bf16hi(qu[2]), bf16hi(qu[3]));
-            d1[1] = make_float4(bf16hi(qu[4]), bf16hi(qu[5]), bf16hi(qu[6]), bf16hi(qu[7]));
+            const int m = (2 * lane) & 15, c = (2 * lane) >> 4;
+#pragma unroll
+            for (int t = 0; t < HG; ++t) {
+                qw[t][m][c] = bf16lo(qu[t]);
+                qw[t][m + 1][c] = bf16hi(qu[t]);
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): this wave's q rows are in LDS
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    // the eight chains over elements i0 .. i0 + 7, each in ascending element order
-    auto chains8 = [&](const float (&k)[D], int i0, float (&a)[HG]) {
 #pragma unroll
-        for (int i = i0; i < i0 + 8; ++i) {
-            const float4 qa = *reinterpret_cast<const float4 *>(&qw[i][0]);
-            const float4 qb2 = *reinterpret_cast<const float4 *>(&qw[i][4]);
-            a[0] = __builtin_fmaf(qa.x, k[i], a[0]);
-            a[1] = __builtin_fmaf(qa.y, k[i], a[1]);
-            a[2] = __builtin_fmaf(qa.z, k[i], a[2]);
-            a[3] = __builtin_fmaf(qa.w, k[i], a[3]);
-            a[4] = __builtin_fmaf(qb2.x, k[i], a[4]);
-            a[5] = __builtin_fmaf(qb2.y, k[i], a[5]);
-            a[6] = __builtin_fmaf(qb2.z, k[i], a[6]);
-            a[7] = __builtin_fmaf(qb2.w, k[i], a[7]);
-        }
+        for (int t = 0; t < HG; ++t)
+#pragma unroll
+            for (int c4 = 0; c4 < NC; c4 += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(&qw[t][lane & 15][c4]);
+                qc[c4][t] = v.x;
+                qc[c4 + 1][t] = v.y;
+                qc[c4 + 2][t] = v.z;
+                qc[c4 + 3][t] = v.w;
+            }
     };
     auto fold = [&](const float (&a)[HG], int nh) {
 #pragma unroll
@@ -113,32 +137,34 @@ __global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(Index
 #pragma unroll
         for (int c = 0; c < D / 8; ++c) kraw[c] = kp[c];
         __builtin_amdgcn_sched_barrier(0);    // keep every key load ahead of the wait for q
-        stage_q(qu);
-        // first head group: each 8-element chunk of the key is converted to fp32 and used as
+        float qc[NC][HG];
+        stage_q(qu, qc);
+        // first head group: each 16-element chunk of the key is converted to fp32 and used as
         // soon as it has arrived, while the later chunks are still in flight
         float k[D];
         float a[HG];
 #pragma unroll
         for (int t = 0; t < HG; ++t) a[t] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const uint4 v = kraw[c];
-            k[8 * c + 0] = bf16lo(v.x); k[8 * c + 1] = bf16hi(v.x);
-            k[8 * c + 2] = bf16lo(v.y); k[8 * c + 3] = bf16hi(v.y);
-            k[8 * c + 4] = bf16lo(v.z); k[8 * c + 5] = bf16hi(v.z);
-            k[8 * c + 6] = bf16lo(v.w); k[8 * c + 7] = bf16hi(v.w);
-            chains8(k, 8 * c, a);
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint4 v = kraw[2 * c + h];
+                float *kk = &k[16 * c + 8 * h];
+                kk[0] = bf16lo(v.x); kk[1] = bf16hi(v.x); kk[2] = bf16lo(v.y); kk[3] = bf16hi(v.y);
+                kk[4] = bf16lo(v.z); kk[5] = bf16hi(v.z); kk[6] = bf16lo(v.w); kk[7] = bf16hi(v.w);
+            }
+            fmac16x8(a, qc[c], &k[16 * c]);
         }
         fold(a, min(HG, G));
         // further head groups reuse the converted key
         for (int h0 = HG; h0 < G; h0 += HG) {
-            __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's reads of the previous group are done
             load_q(g, h0, qu);
-            stage_q(qu);
+            stage_q(qu, qc);
 #pragma unroll
             for (int t = 0; t < HG; ++t) a[t] = 0.0f;
 #pragma unroll
-            for (int c = 0; c < D / 8; ++c) chains8(k, 8 * c, a);
+            for (int c = 0; c < NC; ++c) fmac16x8(a, qc[c], &k[16 * c]);
             fold(a, min(HG, G - h0));
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);       // reads done before the next KV head's staging
