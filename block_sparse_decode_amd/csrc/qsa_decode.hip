@@ -232,7 +232,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     // A column's running max is raised only when a logit exceeds it by more than this
     // (log2 units), so most sub-chunks skip the rescale; P stays <= 2^8 in f16.
     constexpr float kLazy = 8.0f;
-    static_assert((NW - 2) * (NDT + 1) * 64 * 16 <= NW * 32 * D * 2, "merge slots must fit the V staging area");
+    static_assert(NDT * 64 * 16 <= 32 * D * 2, "a wave's published tiles must fit its V staging tile");
+    static_assert(NDT <= NW, "every output tile needs an owner wave");
     static_assert(D / 8 <= 16, "one V row holds at most 16 swizzled chunks");
 
     // One LDS area: the union build's scratch (row-mask bitmap, page-table row, owner of each
@@ -243,7 +244,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     half_t(*vsm)[32 * D] = reinterpret_cast<half_t(*)[32 * D]>(lds_area);
     __shared__ uint32_t u_pm[kMaxUnion];    // page | row mask << 16 | sub-chunks << 24
     __shared__ int32_t u_phys[kMaxUnion];
-    __shared__ float ml_m[NW][16];
+    __shared__ float ml_m[NW][16];         // per wave: column maxima (log2 units)
+    __shared__ float ml_l[NW][16];         // per wave: softmax denominators
     __shared__ uint32_t scan_tmp[NT / 64 + 1];
     __shared__ f16x8 q_lds[KS][64];         // the tile's q operand, in MFMA B-operand lane order
 
@@ -548,109 +550,135 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         u = un;
     }
 
-    // ---- 4. merge the waves in LDS (fixed tree order), then write ------------------
-    if (gq == 0) ml_m[wave][li] = m_col;
-    __syncthreads();                 // all waves are done with their V staging
+    // ---- 4. merge the waves (fixed order); wave w < d/16 finishes output tile w --------
+    // Every wave publishes its column maxima and denominators, and in its own V staging tile
+    // (which no other wave touches) the O^T tiles that other waves own, packed in ascending
+    // tile order without its own. After one barrier, each wave takes the common column max M
+    // and the weights 2^(m_w - M), and the owner of tile w sums that tile over the waves in
+    // ascending wave order, as every wave sums the denominators, so the result does not
+    // depend on which wave does the sum.
     {
-        float M = NEG_INF;
+        float *pub = reinterpret_cast<float *>(vs);
+        if (gq == 0) {
+            ml_m[wave][li] = m_col;
+            ml_l[wave][li] = oacc[NDT][0];
+        }
 #pragma unroll
-        for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_m[w][li]);
-        const float wgt = (M == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(m_col - M);
-#pragma unroll
-        for (int dt = 0; dt <= NDT; ++dt) oacc[dt] *= wgt;
-        m_col = M;                   // common reference max of the column
-    }
-    // Two levels in a fixed order: waves 2 .. NW-1 publish, waves 0 and 1 add the even and
-    // the odd ones in ascending order; then wave 1 publishes and wave 0 adds.
-    // Slot layout [slot][dt][lane] f32x4: every lane moves 16 contiguous bytes.
-    f32x4 *slots = reinterpret_cast<f32x4 *>(&vsm[0][0]);
-    constexpr int kSlot = (NDT + 1) * 64;
-    if (wave >= 2) {
-#pragma unroll
-        for (int dt = 0; dt <= NDT; ++dt) slots[(wave - 2) * kSlot + dt * 64 + lane] = oacc[dt];
-    }
-    __syncthreads();
-    if (wave < 2) {
-        for (int w = wave + 2; w < NW; w += 2) {
-#pragma unroll
-            for (int dt = 0; dt <= NDT; ++dt) oacc[dt] += slots[(w - 2) * kSlot + dt * 64 + lane];
+        for (int dt = 0; dt < NDT; ++dt) {
+            if (dt == wave) continue;
+            const int slot = dt < wave ? dt : dt - 1;
+            *reinterpret_cast<f32x4 *>(pub + (slot * 64 + lane) * 4) = oacc[dt];
         }
     }
     __syncthreads();
-    if (wave == 1) {
+    const bool owns_tile = wave < NDT;
+    f32x4 o_own = oacc[0];          // the merged tile `wave` (owner waves only)
 #pragma unroll
-        for (int dt = 0; dt <= NDT; ++dt) slots[dt * 64 + lane] = oacc[dt];
-    }
-    __syncthreads();
-    if (wave == 0) {
+    for (int dt = 1; dt < NDT; ++dt)
+        if (dt == wave) o_own = oacc[dt];
+    float M = NEG_INF;
 #pragma unroll
-        for (int dt = 0; dt <= NDT; ++dt) oacc[dt] += slots[dt * 64 + lane];
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_m[w][li]);
+    float Lsum = 0.0f;
+    {
+        f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = ml_m[w][li];
+            const float wgt = (mw == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+            Lsum = __builtin_fmaf(wgt, ml_l[w][li], Lsum);
+            if (owns_tile) {
+                f32x4 o;
+                if (w == wave) {
+                    o = o_own;
+                } else {
+                    const int slot = wave < w ? wave : wave - 1;
+                    o = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(&vsm[w][0]) +
+                                                         (slot * 64 + lane) * 4);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wgt, o[i], acc[i]);
+            }
+        }
+        o_own = acc;
     }
-    if (wave != 0) return;
+    m_col = M;
     if (S > 1) {
-        // Publish this split's partial, count it, and let the tile's last split merge.
-        // The partial moves through agent-scope (coherent) stores and loads: each such access
-        // is coherent across the XCDs' L2s on its own, so the handoff needs only the stores'
-        // completion (vmcnt 0) before the count -- not an agent-scope fence, whose L2
+        // Publish this split's partial (each owner its tile, wave 0 the denominators and the
+        // column maxima), count it, and let the tile's last split merge. The partial moves
+        // through agent-scope (coherent) stores and loads: each such access is coherent
+        // across the XCDs' L2s on its own, so the handoff needs only the stores' completion
+        // (vmcnt 0, then a barrier) before the count -- not an agent-scope fence, whose L2
         // writeback and invalidate cost several microseconds per workgroup here.
         constexpr int PF = decode_part_floats(D);
         constexpr int kOff = (NDT + 1) * 64 * 4;
         float *tile_part = prm.part + (int64_t)tile * S * PF;
         float *mine = tile_part + (int64_t)s * PF;
-#pragma unroll
-        for (int dt = 0; dt <= NDT; ++dt)
+        if (owns_tile) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                __hip_atomic_store(mine + (dt * 4 + i) * 64 + lane, oacc[dt][i], __ATOMIC_RELAXED,
+                __hip_atomic_store(mine + (wave * 4 + i) * 64 + lane, o_own[i], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(mine + kOff + lane, m_col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): the partial's stores are complete
-        uint32_t done = 0u;
-        if (lane == 0) done = __hip_atomic_fetch_add(prm.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        done = __builtin_amdgcn_readfirstlane(done);
-        if (done != (uint32_t)(S - 1)) return;
-        // the last split: every other partial's stores completed before its count
-        float M = NEG_INF;
+        }
+        if (wave == 0) {
+            __hip_atomic_store(mine + (NDT * 4) * 64 + lane, Lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + kOff + lane, m_col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): this wave's partial stores are complete
+        __syncthreads();
+        if (wave == 0) {
+            uint32_t done = 0u;
+            if (lane == 0) done = __hip_atomic_fetch_add(prm.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            done = __builtin_amdgcn_readfirstlane(done);
+            if (lane == 0) scan_tmp[1] = done;
+        }
+        __syncthreads();
+        if (scan_tmp[1] != (uint32_t)(S - 1)) return;
+        // the last split: every other partial's stores completed before its count; each wave
+        // takes the common max and the denominator over the splits, and its owned tile
+        float Ms = NEG_INF;
         for (int sp = 0; sp < S; ++sp)
-            M = fmaxf(M, sp == s ? m_col
-                                 : __hip_atomic_load(tile_part + (int64_t)sp * PF + kOff + lane, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
-        f32x4 acc[NDT + 1];
-#pragma unroll
-        for (int dt = 0; dt <= NDT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            Ms = fmaxf(Ms, sp == s ? m_col
+                                   : __hip_atomic_load(tile_part + (int64_t)sp * PF + kOff + lane, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+        f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+        float Ls = 0.0f;
         for (int sp = 0; sp < S; ++sp) {         // ascending split order
             const float *part = tile_part + (int64_t)sp * PF;
-            f32x4 o[NDT + 1];
-            float m;
+            f32x4 o;
+            float m, l;
             if (sp == s) {
-#pragma unroll
-                for (int dt = 0; dt <= NDT; ++dt) o[dt] = oacc[dt];
+                o = o_own;
                 m = m_col;
+                l = Lsum;
             } else {
-#pragma unroll
-                for (int dt = 0; dt <= NDT; ++dt)
+                if (owns_tile) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        o[dt][i] = __hip_atomic_load(part + (dt * 4 + i) * 64 + lane, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
+                        o[i] = __hip_atomic_load(part + (wave * 4 + i) * 64 + lane, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                }
                 m = __hip_atomic_load(part + kOff + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                l = __hip_atomic_load(part + (NDT * 4) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            const float wgt = (m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+            const float wgt = (m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(m - Ms);
+            Ls = __builtin_fmaf(wgt, l, Ls);
+            if (owns_tile) {
 #pragma unroll
-            for (int dt = 0; dt <= NDT; ++dt) acc[dt] += wgt * o[dt];
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wgt, o[i], acc[i]);
+            }
         }
-#pragma unroll
-        for (int dt = 0; dt <= NDT; ++dt) oacc[dt] = acc[dt];
-        m_col = M;
-        if (lane == 0) __hip_atomic_store(prm.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        o_own = acc;
+        Lsum = Ls;
+        m_col = Ms;
+        if (wave == 0 && lane == 0) __hip_atomic_store(prm.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (!colv) return;
     const int row = r0 + jc, head = g * G + (col - jc * G);
-    const float L = oacc[NDT][0];
-    const float sc = (L > 0.0f) ? prm.v_global / L : 0.0f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-        f32x4 o = oacc[dt] * sc;
+    const float sc = (Lsum > 0.0f) ? prm.v_global / Lsum : 0.0f;
+    if (owns_tile) {
+        const int dt = wave;
+        f32x4 o = o_own * sc;
         if (prm.gate) {
             // the gated epilogue: out * sigmoid(gate), one rounding to bf16 after the product
             const uint2 gr = *reinterpret_cast<const uint2 *>(prm.gate + ((int64_t)row * prm.Hq + head) * D +
@@ -665,8 +693,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         packed.y = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
         *reinterpret_cast<uint2 *>(prm.out + ((int64_t)row * prm.Hq + head) * D + dt * 16 + gq * 4) = packed;
     }
-    if (gq == 0 && prm.lse)
-        prm.lse[(int64_t)row * prm.Hq + head] = (L > 0.0f) ? (m_col + __log2f(L)) * 0.69314718055994531f : NEG_INF;
+    if (wave == 0 && gq == 0 && prm.lse)
+        prm.lse[(int64_t)row * prm.Hq + head] = (Lsum > 0.0f) ? (m_col + __log2f(Lsum)) * 0.69314718055994531f : NEG_INF;
 }
 
 template <int D, int SELC>

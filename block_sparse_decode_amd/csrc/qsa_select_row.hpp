@@ -10,7 +10,10 @@
 //  1. Non-candidates get key 0 (every candidate key is >= 0x00800000).
 //  2. The k-th largest key T is found bit by bit, most significant first: a bit is kept
 //     when at least k keys are >= the prefix with that bit set. Each count is a ballot per
-//     register slot and a scalar popcount, exact in any order.
+//     register slot and a scalar popcount, exact in any order. The search starts at the
+//     highest bit in which the candidates differ (the bits above it are common to all of
+//     them, so T has them too), and stops early when exactly k keys are >= the prefix:
+//     those k keys are then the top k, with no tie across the boundary.
 //  3. Keys above T are all taken. Of the keys equal to T, the highest page indices fill
 //     the remaining slots, ranked by a wave suffix count of ties.
 //  4. The union with the window is compacted in ascending page order by a wave prefix
@@ -39,6 +42,22 @@ __device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[C], uint
         for (int i = 0; i < 8; ++i) c += (uint32_t)__builtin_popcountll(m[i]);
     }
     return c;
+}
+
+// Bitwise AND / OR over the 64 lanes (all active): DPP within each 16-lane row (swap lane
+// pairs, then pairs of pairs, then the mirrored half row and the mirrored row), then the
+// four rows' results through readlane.
+template <bool OR>
+__device__ __forceinline__ uint32_t wave_bitreduce(uint32_t x)
+{
+    auto op = [](uint32_t a, uint32_t b) { return OR ? (a | b) : (a & b); };
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true));    // quad_perm [1,0,3,2]
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, true));   // row_half_mirror
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, true));   // row_mirror
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return op(op(r0, r1), op(r2, r3));
 }
 
 // The row's scores as raw bits, lane l holding columns l*C .. l*C + C - 1 (0 past MP).
@@ -96,13 +115,33 @@ __device__ __forceinline__ void select_row_keys(uint32_t (&key)[C], int n, int k
     } else if (ncand <= k) {
         T = 0u;                           // every candidate (key > 0) is taken
     } else {
-        T = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t t = T | (1u << bit);
-            if (wave_count_ge<C>(key, t) >= k) T = t;
+        // the bits above the highest one in which the candidates differ
+        uint32_t kand = 0xffffffffu, kor = 0u;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            kand &= key[i] != 0u ? key[i] : 0xffffffffu;
+            kor |= key[i];
         }
-        const uint32_t ngt = wave_count_ge<C>(key, T + 1u);   // T < 2^32 - 1: T is a finite score's key
-        krem = k - ngt;                   // >= 1
+        kand = wave_bitreduce<false>(kand);
+        kor = wave_bitreduce<true>(kor);
+        const uint32_t diff = kand ^ kor;
+        const int hb = diff != 0u ? 31 - __builtin_clz(diff) : -1;
+        T = hb >= 0 ? kand & ~((2u << hb) - 1u) : kand;   // hb = -1: all candidates are equal
+        // the loop state stays scalar: `left` counts the bits still to decide
+        int left = hb + 1;
+        uint32_t bitv = hb >= 0 ? 1u << hb : 0u;
+        for (; left > 0; --left, bitv >>= 1) {
+            const uint32_t t = T | bitv;
+            const uint32_t c = wave_count_ge<C>(key, t);
+            if (c >= k) T = t;
+            if (c == k) break;
+        }
+        if (left > 0) {
+            T -= 1u;                      // the k keys >= the prefix are exactly the keys > T
+        } else {
+            const uint32_t ngt = wave_count_ge<C>(key, T + 1u);   // T < 2^32 - 1: T is a finite score's key
+            krem = k - ngt;               // >= 1
+        }
     }
 
     // 3. ties at T go to the highest pages: rank each tie by the ties at higher pages (later

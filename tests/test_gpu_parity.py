@@ -226,7 +226,7 @@ def test_workspace_reused_across_split_counts():
         assert int(ws[:tiles * 4].count_nonzero().item()) == 0, f"counters left non-zero after splits={sp}"
 
 
-FUSED_CASES = [(c, sp) for c in ATT_SMALL[:4] for sp in (0, 3)] + [(n, 0) for n in CONFIG_NAMES] + [
+FUSED_CASES = [(c, sp) for c in ATT_SMALL[:4] for sp in (0, 1, 3)] + [(n, 0) for n in CONFIG_NAMES] + [
     (synth.Config("f_wide_table", 3, 2, 16, 2, 128, 64, (300, 5000), 6, 2, seed=401, max_pages=1500), 0),
     (synth.Config("f_mp1024", 2, 4, 32, 4, 64, 64, (900, 60000), 8, 1, seed=402, invalid_frac=0.1), 2),
 ]
@@ -279,8 +279,11 @@ def test_attention_full_size_sampled(name):
 
 # --------------------------------------------------------------------- edge cases --
 
-def test_attention_edge_selections():
-    """Empty rows, pages past a row's length, duplicates, invalid pages, out-of-range ids."""
+@pytest.mark.parametrize("splits", [1, 3])
+def test_attention_edge_selections(splits):
+    """Empty rows, pages past a row's length, duplicates, invalid pages, out-of-range ids.
+    With one split, rows that leave out a page of their window take the path without
+    early window units."""
     cfg = synth.Config("edge", 4, 4, 16, 2, 128, 64, (10, 700), 4, 2, seed=301, invalid_frac=0.2)
     w = workload(cfg)
     base = oracle.select_w(w, oracle.index_scores(w))
@@ -288,7 +291,8 @@ def test_attention_edge_selections():
     sel[0] = -1                                    # empty row
     sel[1, :3] = [0, 0, 0]                          # duplicates count once
     sel[2, -1] = w.MP - 1                           # a page at/after the row's end
-    b, st = _run(w, num_splits=3, sel_override=sel)
+    sel[3, -2:] = -1                                # the window left out
+    b, st = _run(w, num_splits=splits, sel_override=sel)
     ref_out, ref_lse = oracle.attention(w, sel)
     _check_attention(_u16(st.out), st.lse.cpu().numpy(), ref_out, ref_lse, "edge")
     out0 = _u16(st.out)[0]
@@ -306,8 +310,10 @@ def test_attention_edge_selections():
     _check_attention(_u16(st.out), st.lse.cpu().numpy(), ref_out, ref_lse, "edge-oor")
 
 
-def test_short_request_and_bad_page_ids():
-    """A request shorter than its rows, and a page-table entry >= NP (treated as -1, flagged)."""
+@pytest.mark.parametrize("splits", [1, 2])
+def test_short_request_and_bad_page_ids(splits):
+    """A request shorter than its rows, and a page-table entry >= NP (treated as -1, flagged),
+    with one split inside the pages every row's window holds."""
     cfg = synth.Config("short", 3, 4, 8, 2, 64, 64, (1, 300), 3, 1, seed=302)
     w = workload(cfg)
     w = dataclasses.replace(w)
@@ -316,7 +322,7 @@ def test_short_request_and_bad_page_ids():
     w.page_table = w.page_table.copy()
     n0 = -(-int(w.seq_lens[0]) // 64)
     w.page_table[0, n0 - 1] = w.NP + 3              # out-of-range physical id in row 0's window
-    b, st = _run(w, num_splits=2)
+    b, st = _run(w, num_splits=splits)
     ref_s = oracle.index_scores(w)
     assert np.array_equal(st.scores.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
     sel = st.selected.cpu().numpy()
