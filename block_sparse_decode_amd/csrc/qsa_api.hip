@@ -272,6 +272,11 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     prm.tile_cols = tile_cols(sh);
     if (decode_tiles(sh) * splits > (int64_t)1 << 30) return QSA_ERR_UNSUPPORTED;
     prm.tiles = (int)decode_tiles(sh);
+    prm.div_splits = FastDiv::make((uint32_t)splits);
+    prm.div_ctiles = FastDiv::make((uint32_t)prm.col_tiles);
+    prm.div_htiles = FastDiv::make((uint32_t)(prm.Hkv * prm.col_tiles));
+    prm.div_group = FastDiv::make((uint32_t)(prm.Hq / prm.Hkv));
+    prm.div_kw = FastDiv::make((uint32_t)(KW > 0 ? KW : 1));
     prm.qk_scale_log2 = (float)qk;
     prm.v_global = pg->v_global;
     prm.gate = gate;

@@ -252,31 +252,33 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     // work item i = tile * S + split, tiles numbered (request, KV head, column tile); XCD x
     // (the dispatcher's linear id mod 8) takes the contiguous items [x * per, (x + 1) * per)
     const int S = prm.splits;
-    const int64_t n_items = (int64_t)prm.tiles * S;
-    const int64_t per = (n_items + kXcds - 1) / kXcds;
-    const int wg = blockIdx.x;
-    const int64_t item = (int64_t)(wg % kXcds) * per + wg / kXcds;
+    // (tiles * S < 2^30, so the item arithmetic fits 32 bits; the divisors are the host's)
+    const uint32_t n_items = (uint32_t)prm.tiles * (uint32_t)S;
+    const uint32_t per = (n_items + kXcds - 1) / kXcds;
+    const uint32_t wg = blockIdx.x;
+    const uint32_t item = (wg % kXcds) * per + wg / kXcds;
     if (item >= n_items) return;
-    const int tile = (int)(item / S), s = (int)(item - (int64_t)tile * S);
+    const int tile = (int)fast_div(item, prm.div_splits), s = (int)item - tile * S;
     const int T = prm.col_tiles;
     const int HT = prm.Hkv * T;
-    const int b = tile / HT;
-    const int g = (tile - b * HT) / T, ct = tile - b * HT - g * T;
+    const int b = (int)fast_div((uint32_t)tile, prm.div_htiles);
+    const int g = (int)fast_div((uint32_t)(tile - b * HT), prm.div_ctiles), ct = tile - b * HT - g * T;
+    // the request's row range and length, both loads issued before either is waited on
+    const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
+    const int64_t Lb = prm.seq_lens[b];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform, so in SGPRs
     const int gq = lane >> 4, li = lane & 15;
-    const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
     const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, tid == 0 && s == 0 && tile == b * HT);
     const int Rb = r1 - r0;         // the request's own row count fixes each row's length
-    const int G = prm.Hq / prm.Hkv;
+    const int G = (int)prm.div_group.d;
     const int TW = prm.tile_cols;   // this tile: columns col0 .. col0 + TW - 1 of the request's R x G
     const int col0 = ct * TW;
     if (col0 >= R * G) return;
-    const int j_lo = col0 / G;
-    const int j_hi = min(R - 1, (col0 + TW - 1) / G);
+    const int j_lo = (int)fast_div((uint32_t)col0, prm.div_group);
+    const int j_hi = min(R - 1, (int)fast_div((uint32_t)(col0 + TW - 1), prm.div_group));
     const int nrow = j_hi - j_lo + 1;                // rows of this tile (<= 4)
     const int MP = prm.MP, P = prm.P, KW = prm.KW;
-    const int64_t Lb = prm.seq_lens[b];
 
     // ---- 1. union of the tile's rows' selected pages; the q operand ------------------
     // All threads stage this request's page-table row in LDS (scratch in the V staging
@@ -288,6 +290,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     // appends it, with ballot counts for the positions, so no workgroup barrier is needed.
     // Meanwhile the last wave converts q into the MFMA B operand in LDS. Union order: by
     // first listing (rows in order), a function of the input alone.
+    // A one-row tile with the selection fused in takes a shorter way: its selecting wave
+    // holds the page-table entries of its columns in registers beside the score keys and
+    // writes the union itself (the selected pages with a valid physical page, ascending, as
+    // the union build would list them), so neither the LDS copy of the page table nor the
+    // union build and its barrier are needed.
     const int nwords = ((MP + 3) / 4 + 3) & ~3;
     uint32_t *bm = reinterpret_cast<uint32_t *>(lds_area);
     int32_t *pt_row = reinterpret_cast<int32_t *>(bm + nwords);
@@ -296,6 +303,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     constexpr int kSelPerLane = kMaxUnion / 64;
     int selp[kSelPerLane];
     int32_t *sel_lds = reinterpret_cast<int32_t *>(u_pm);   // the selections, before the union
+    const bool one_row = SELC > 0 && nrow == 1;
 
     // The independent global loads go first, so that no wave waits for one of them before
     // issuing the next: each selecting wave's score row (or wave 0's selection rows), the
@@ -307,16 +315,31 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
             const int idx = lane + i * 64;
             selp[i] = -1;
             if (wave == 0 && idx < nent) {
-                const int jr = idx / KW;
+                const int jr = (int)fast_div((uint32_t)idx, prm.div_kw);
                 selp[i] = prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)];
             }
         }
     } else {
         if (wave < nrow) select_row_load<SELC, false>(prm.scores + (int64_t)(r0 + j_lo + wave) * MP, MP, skey);
     }
+    // one-row tiles: the page-table entries of the selecting lane's columns
+    int ptv[SELC > 0 ? SELC : 1];
+    if constexpr (SELC > 0) {
+        if (one_row && wave == 0) {
+            // as the score loads: one clamped load per column, no branch; only selected
+            // columns, all inside the row, are read
+            const int c0 = lane * SELC;
+            const int32_t *ptr = prm.page_table + (int64_t)b * MP;
+#pragma unroll
+            for (int i = 0; i < SELC; ++i) {
+                const int c = c0 + i;
+                ptv[i] = ptr[c < MP ? c : 0];
+            }
+        }
+    }
     // this lane's query column
     const int col = col0 + li;
-    const int jc = col / G;                           // row of this lane's column
+    const int jc = (int)fast_div((uint32_t)col, prm.div_group);   // row of this lane's column
     const bool colv = li < TW && jc < R;              // false: padding column
     uint4 qraw[KS];
 #pragma unroll
@@ -327,18 +350,97 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qraw[ks] = qp[ks];
     }
-    for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
-    for (int p = tid; p < MP; p += NT) {
-        pt_row[p] = prm.page_table[(int64_t)b * MP + p];
-        owner[p] = 0xffffffffu;
+    if (!one_row) {
+        for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
+        for (int p = tid; p < MP; p += NT) {
+            pt_row[p] = prm.page_table[(int64_t)b * MP + p];
+            owner[p] = 0xffffffffu;
+        }
     }
     if constexpr (SELC > 0) {
-        // wave w selects the tile's row j_lo + w, into LDS
-        if (wave < nrow)
+        if (one_row) {
+            if (wave == 0) {
+                // The row's selection (into LDS, for the tile where the row starts, of KV
+                // head 0 and split 0, to publish after the barrier) and the union: the selected pages whose
+                // page-table entry is a valid physical page. Both lists are compacted without
+                // branches: one prefix scan gives both positions (selection count in the low
+                // half, union count in the high half), and a column that is in neither list
+                // writes a dump slot of its lane.
+                const RowGeom geo = row_geom(Lb, Rb, j_lo, prm.log2P, MP);
+                const uint32_t take = (uint32_t)select_row_take<SELC>(skey, geo.pages, prm.k, prm.W);
+                const uint32_t npc = prm.NP < ((int64_t)1 << 31) ? (uint32_t)prm.NP : 0x80000000u;
+                uint32_t ok = 0u, bad = 0u;
+#pragma unroll
+                for (int i = 0; i < SELC; ++i) {
+                    const uint32_t valid = (uint32_t)((uint32_t)ptv[i] < npc);
+                    const uint32_t invalid = (uint32_t)(ptv[i] != -1) & (valid ^ 1u);
+                    ok |= valid << i;
+                    bad |= invalid << i;
+                }
+                ok &= take;
+                if (bad & take) set_error(prm.err, QSA_DEVERR_PAGE_ID);
+                const uint32_t cnt = (uint32_t)__builtin_popcount(take) | ((uint32_t)__builtin_popcount(ok) << 16);
+                const uint32_t incl = wave_inclusive_scan(cnt);
+                const uint32_t excl = incl - cnt;
+                const int c0 = lane * SELC;
+                const int lenc = (int)min(geo.len, (int64_t)MP << prm.log2P);
+                int32_t *sel_row = reinterpret_cast<int32_t *>(lds_area);   // KW entries, then dump slots
+                const int sel_dump = KW + lane, u_dump = kMaxUnion - 64 + lane;
+#pragma unroll
+                for (int i = 0; i < SELC; ++i) {
+                    const uint32_t below = (1u << i) - 1u;
+                    const int p = c0 + i;
+                    const int spos = (int)((excl & 0xffffu) + (uint32_t)__builtin_popcount(take & below));
+                    const int upos = (int)((excl >> 16) + (uint32_t)__builtin_popcount(ok & below));
+                    const int vis = lenc - (p << prm.log2P);
+                    const int nc = vis >= P ? P / 32 : (vis + 31) / 32;
+                    sel_row[(take >> i) & 1u ? spos : sel_dump] = p;
+                    const int ui = (ok >> i) & 1u ? upos : u_dump;
+                    u_pm[ui] = (uint32_t)p | (1u << 16) | ((uint32_t)nc << 24);
+                    u_phys[ui] = ptv[i];
+                }
+                if (lane == 63) {
+                    scan_tmp[0] = incl >> 16;
+                    scan_tmp[1] = incl & 0xffffu;
+                }
+            }
+        } else if (wave < nrow) {
+            // wave w selects the tile's row j_lo + w, into LDS
             select_row_keys<SELC>(skey, row_geom(Lb, Rb, j_lo + wave, prm.log2P, MP).pages, prm.k, prm.W,
                                   sel_lds + wave * KW);
+        }
+    }
+    if (wave == NW - 1) {
+        bool qbad = false;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            f16x8 v = {};
+            if (colv) {
+                const uint4 raw = qraw[ks];
+                const float f[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
+                                    bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
+#pragma unroll
+                for (int t = 0; t < 8; ++t) qbad |= !(fabsf(f[t]) <= 65504.0f);
+                const f16x2 h0 = {(half_t)f[0], (half_t)f[1]}, h1 = {(half_t)f[2], (half_t)f[3]};
+                const f16x2 h2 = {(half_t)f[4], (half_t)f[5]}, h3 = {(half_t)f[6], (half_t)f[7]};
+                v = __builtin_shufflevector(__builtin_shufflevector(h0, h1, 0, 1, 2, 3),
+                                            __builtin_shufflevector(h2, h3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            q_lds[ks][lane] = v;
+        }
+        if (qbad) set_error(prm.err, QSA_DEVERR_Q_RANGE);
     }
     __syncthreads();
+    if (one_row && wave == 0 && g == 0 && s == 0 && col0 <= j_lo * G) {
+        // the row's selection, ascending, then -1 padding (before this wave's V staging
+        // reuses the LDS copy)
+        const int32_t *sel_row = reinterpret_cast<const int32_t *>(lds_area);
+        const int nsel = (int)scan_tmp[1];
+        int32_t *dst = prm.selected + (int64_t)(r0 + j_lo) * KW;
+        for (int i = lane; i < KW; i += 64) dst[i] = i < nsel ? sel_row[i] : -1;
+        wave_lds_fence();
+    }
+    if (!one_row) {
     if (wave == 0) {
         if constexpr (SELC > 0) {
             // this workgroup publishes the rows that start in its tile (KV head 0, split 0)
@@ -349,7 +451,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
                 if (i * 64 >= nent) break;
                 if (idx < nent) {
                     selp[i] = sel_lds[idx];
-                    const int jr = idx / KW;
+                    const int jr = (int)fast_div((uint32_t)idx, prm.div_kw);
                     if (g == 0 && s == 0 && col0 <= (j_lo + jr) * G)
                         prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)] = selp[i];
                 }
@@ -363,7 +465,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
             const int idx = lane + i * 64;
             if (i * 64 >= nent) break;
             if (idx >= nent) continue;
-            const int jr = idx / KW;
+            const int jr = (int)fast_div((uint32_t)idx, prm.div_kw);
             const int p = selp[i];
             if (p < -1 || p >= MP) {
                 set_error(prm.err, QSA_DEVERR_SELECTED);
@@ -402,27 +504,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
             nu += (uint32_t)__builtin_popcountll(bal);
         }
         if (lane == 0) scan_tmp[0] = nu;
-    } else if (wave == NW - 1) {
-        bool qbad = false;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            f16x8 v = {};
-            if (colv) {
-                const uint4 raw = qraw[ks];
-                const float f[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
-                                    bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
-#pragma unroll
-                for (int t = 0; t < 8; ++t) qbad |= !(fabsf(f[t]) <= 65504.0f);
-                const f16x2 h0 = {(half_t)f[0], (half_t)f[1]}, h1 = {(half_t)f[2], (half_t)f[3]};
-                const f16x2 h2 = {(half_t)f[4], (half_t)f[5]}, h3 = {(half_t)f[6], (half_t)f[7]};
-                v = __builtin_shufflevector(__builtin_shufflevector(h0, h1, 0, 1, 2, 3),
-                                            __builtin_shufflevector(h2, h3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-            q_lds[ks][lane] = v;
-        }
-        if (qbad) set_error(prm.err, QSA_DEVERR_Q_RANGE);
     }
-    __syncthreads();                 // union list and q ready; the scratch area becomes V staging
+    __syncthreads();                 // union list ready; the scratch area becomes V staging
+    }
     const uint32_t U = scan_tmp[0];
     // The lane's bit in a page's row mask (bit 8, always set below, for a padding column) and
     // its row's visible length, at most MP pages. A padding column has a zero q, so it sees
@@ -434,7 +518,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     // ---- 3. online softmax over this wave's sub-chunks, the next one in flight -----
     const int lc = prm.log2P - 5;                   // log2(sub-chunks per page)
     const int NU = (int)U << lc;
-    const int u_lo = (int)(((int64_t)s * NU) / S), u_hi = (int)(((int64_t)(s + 1) * NU) / S);
+    const int u_lo = S == 1 ? 0 : (int)(((int64_t)s * NU) / S), u_hi = S == 1 ? NU : (int)(((int64_t)(s + 1) * NU) / S);
     const float c1 = prm.qk_scale_log2;
     const float NEG_INF = -__builtin_inff();
 

@@ -8,6 +8,29 @@
 
 namespace qsa {
 
+// Division by a divisor fixed for the whole launch, as a multiply and a shift (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, n / d = (umulhi(n, m) + n) >> l for
+// every 0 <= n < 2^31 (the sum then fits 32 bits). The host fills it in.
+struct FastDiv {
+    uint32_t d, m, l;
+
+    static FastDiv make(uint32_t d)
+    {
+        FastDiv f;
+        f.d = d;
+        uint32_t l = 0;
+        while (l < 31 && (1u << l) < d) ++l;
+        f.l = l;
+        f.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+        return f;
+    }
+};
+
+// n / f.d for 0 <= n < 2^31 (f taken by value, so that a kernel argument's copy is not
+// addressed)
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.l; }
+
 struct IndexParams {
     const int32_t *page_table;
     const int32_t *seq_lens;
@@ -49,6 +72,7 @@ struct DecodeParams {
     int64_t NP;
     int N, MP, P, log2P, KW, Hq, Hkv, rmax, splits, col_tiles, tiles;
     int tile_cols;            // query columns (rows x q heads of one KV head) per tile, <= 16
+    FastDiv div_splits, div_ctiles, div_htiles, div_group, div_kw;   // S, col_tiles, Hkv * col_tiles, Hq / Hkv, k + W
     int k, W;                 // selection fused in only
     float qk_scale_log2;      // sm_scale * k_global * log2(e)
     float v_global;

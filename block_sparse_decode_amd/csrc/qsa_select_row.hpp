@@ -74,26 +74,25 @@ __device__ __forceinline__ void select_row_load(const float *srow, int MP, uint3
             key[i] = c0 + i < MP ? __float_as_uint(__hip_atomic_load(srow + c0 + i, __ATOMIC_RELAXED,
                                                                      __HIP_MEMORY_SCOPE_AGENT))
                                  : 0u;
-    } else if ((MP & 3) == 0 && c0 + C <= MP) {
-#pragma unroll
-        for (int i = 0; i < C; i += 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(srow + c0 + i);
-            key[i] = __float_as_uint(v.x); key[i + 1] = __float_as_uint(v.y);
-            key[i + 2] = __float_as_uint(v.z); key[i + 3] = __float_as_uint(v.w);
-        }
     } else {
+        // one load per column, the address clamped into the row: no branch and no use of the
+        // values here (either would make the compiler wait for the loads on the spot), so every
+        // load issues before the first is waited on. Columns past the row are never
+        // candidates (they lie past the row's pages), so their values are never read.
 #pragma unroll
-        for (int i = 0; i < C; ++i) key[i] = c0 + i < MP ? __float_as_uint(srow[c0 + i]) : 0u;
+        for (int i = 0; i < C; ++i) {
+            const int c = c0 + i;
+            key[i] = __float_as_uint(srow[c < MP ? c : 0]);
+        }
     }
 }
 
-// The selection from the loaded score bits. n: the row's visible pages; dst: the row's
-// k + W output slots.
+// The selection from the loaded score bits, as a mask per lane: bit i set when column
+// lane * C + i is selected. n: the row's visible pages. (`key` is overwritten.)
 template <int C>
-__device__ __forceinline__ void select_row_keys(uint32_t (&key)[C], int n, int k_, int W, int32_t *dst)
+__device__ __forceinline__ uint64_t select_row_take(uint32_t (&key)[C], int n, int k_, int W)
 {
     const int lane = threadIdx.x & 63;
-    const int KW = k_ + W;
     const int wlo = n - W > 0 ? n - W : 0;
     const int c0 = lane * C;
 
@@ -164,7 +163,16 @@ __device__ __forceinline__ void select_row_keys(uint32_t (&key)[C], int n, int k
         if (t) take |= 1ull << i;
     }
 
-    // 4. ascending compaction, then -1 padding
+    return take;
+}
+
+// 4. ascending compaction of a selection mask into the row's KW = k + W slots, then -1
+//    padding.
+template <int C>
+__device__ __forceinline__ void select_row_emit(uint64_t take, int KW, int32_t *dst)
+{
+    const int lane = threadIdx.x & 63;
+    const int c0 = lane * C;
     const uint32_t cnt_lane = (uint32_t)__builtin_popcountll(take);
     const uint32_t incl = wave_inclusive_scan(cnt_lane);
     const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
@@ -177,6 +185,14 @@ __device__ __forceinline__ void select_row_keys(uint32_t (&key)[C], int n, int k
         }
     }
     for (int i = (int)total + lane; i < KW; i += 64) dst[i] = -1;
+}
+
+// The selection from the loaded score bits. n: the row's visible pages; dst: the row's
+// k + W output slots.
+template <int C>
+__device__ __forceinline__ void select_row_keys(uint32_t (&key)[C], int n, int k_, int W, int32_t *dst)
+{
+    select_row_emit<C>(select_row_take<C>(key, n, k_, W), k_ + W, dst);
 }
 
 // srow: the row's MP scores; n: the row's visible pages; dst: the row's k + W output slots.
