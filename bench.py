@@ -401,6 +401,8 @@ def main():
     gate = torch.from_numpy(synth.bf16_bits_from_f32(gen.standard_normal(w.q.shape, dtype=np.float32)).view(
         np.int16)).to(dev)
     gsteps = {id(st): Step(st.b, num_splits=args.splits, gate=gate) for st in steps}
+    for st in steps:
+        gsteps[id(st)].scores.copy_(st.scores)      # the same scores, so the same selections
     gated_us = stage_us(lambda st: gsteps[id(st)].select_decode_call(stream))
     w8 = synth.generate(w.cfg.with_(kv_format="fp8", name=w.cfg.name + "_fp8"))
     base8 = DeviceBatch.upload(w8, dev)
