@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
             }
         }
     } else {
-        if (wave < nrow) select_row_load<SELC, false>(prm.scores + (int64_t)(r0 + j_lo + wave) * MP, MP, skey);
+        if (wave < nrow) select_row_load<SELC>(prm.scores + (int64_t)(r0 + j_lo + wave) * MP, MP, skey);
     }
     // one-row tiles: the page-table entries of the selecting lane's columns
     int ptv[SELC > 0 ? SELC : 1];

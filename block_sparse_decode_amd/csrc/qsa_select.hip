@@ -18,7 +18,7 @@ __global__ __launch_bounds__(64) void select_topk_kernel(SelectParams prm)
     if (j >= R) return;
     const int row = r0 + j;
     const RowGeom geo = row_geom(prm.seq_lens[b], r1 - r0, j, prm.log2P, prm.MP);
-    select_row<C, false>(prm.scores + (int64_t)row * prm.MP, prm.MP, geo.pages, prm.k, prm.W,
+    select_row<C>(prm.scores + (int64_t)row * prm.MP, prm.MP, geo.pages, prm.k, prm.W,
                          prm.selected + (int64_t)row * (prm.k + prm.W));
 }
 

@@ -60,30 +60,20 @@ __device__ __forceinline__ uint32_t wave_bitreduce(uint32_t x)
     return op(op(r0, r1), op(r2, r3));
 }
 
-// The row's scores as raw bits, lane l holding columns l*C .. l*C + C - 1 (0 past MP).
-// Split from the selection itself so that a caller can issue these loads early.
-// COHERENT: the scores were written by other workgroups of the same launch, so they are
-// read with agent-scope loads.
-template <int C, bool COHERENT>
+// The row's scores as raw bits, lane l holding columns l*C .. l*C + C - 1. Split from the
+// selection itself so that a caller can issue these loads early. One load per column, with the
+// address clamped into the row: no branch and no use of the values here (either would make the
+// compiler wait for the loads on the spot), so every load issues before the first is waited
+// on. Columns past the row are never candidates (they lie past the row's pages), so their
+// values are never read.
+template <int C>
 __device__ __forceinline__ void select_row_load(const float *srow, int MP, uint32_t (&key)[C])
 {
     const int c0 = (threadIdx.x & 63) * C;
-    if constexpr (COHERENT) {
 #pragma unroll
-        for (int i = 0; i < C; ++i)
-            key[i] = c0 + i < MP ? __float_as_uint(__hip_atomic_load(srow + c0 + i, __ATOMIC_RELAXED,
-                                                                     __HIP_MEMORY_SCOPE_AGENT))
-                                 : 0u;
-    } else {
-        // one load per column, the address clamped into the row: no branch and no use of the
-        // values here (either would make the compiler wait for the loads on the spot), so every
-        // load issues before the first is waited on. Columns past the row are never
-        // candidates (they lie past the row's pages), so their values are never read.
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int c = c0 + i;
-            key[i] = __float_as_uint(srow[c < MP ? c : 0]);
-        }
+    for (int i = 0; i < C; ++i) {
+        const int c = c0 + i;
+        key[i] = __float_as_uint(srow[c < MP ? c : 0]);
     }
 }
 
@@ -196,11 +186,11 @@ __device__ __forceinline__ void select_row_keys(uint32_t (&key)[C], int n, int k
 }
 
 // srow: the row's MP scores; n: the row's visible pages; dst: the row's k + W output slots.
-template <int C, bool COHERENT>
+template <int C>
 __device__ __forceinline__ void select_row(const float *srow, int MP, int n, int k_, int W, int32_t *dst)
 {
     uint32_t key[C];
-    select_row_load<C, COHERENT>(srow, MP, key);
+    select_row_load<C>(srow, MP, key);
     select_row_keys<C>(key, n, k_, W, dst);
 }
 

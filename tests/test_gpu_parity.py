@@ -333,6 +333,36 @@ def test_short_request_and_bad_page_ids(splits):
     assert err & q.QSA_DEVERR_PAGE_ID and err & q.QSA_DEVERR_SEQ_LEN
 
 
+@pytest.mark.parametrize("splits", [1, 2])
+def test_fused_bad_page_ids(splits):
+    """The selection fused into the attention launch (one-row tiles: the selecting wave builds the
+    union itself) with -1 entries and a page-table entry >= NP inside a row's window: the same
+    selection rows and outputs as the composed calls, the oracle's attention, and the PAGE_ID bit."""
+    cfg = synth.Config("fused_bad", 3, 1, 8, 2, 64, 64, (300, 2000), 4, 2, seed=303, invalid_frac=0.15)
+    w = dataclasses.replace(workload(cfg))
+    w.page_table = w.page_table.copy()
+    n1 = -(-int(w.seq_lens[1]) // 64)
+    w.page_table[1, n1 - 1] = w.NP + 7              # out-of-range physical id in request 1's window
+    b = DeviceBatch.upload(w)
+    ref = Step(b, num_splits=splits, fused=False)
+    ref()
+    torch.cuda.synchronize()
+    err_ref = int(b.error_word[0].item())
+    b.error_word.zero_()
+    fus = Step(b, num_splits=splits, fused=True)
+    fus.selected.fill_(-7)
+    fus()
+    torch.cuda.synchronize()
+    err = int(b.error_word[0].item())
+    ref_s = oracle.index_scores(w)
+    ref_sel = oracle.select_w(w, ref_s)
+    assert np.array_equal(fus.selected.cpu().numpy(), ref_sel)
+    assert torch.equal(fus.out, ref.out) and torch.equal(fus.lse, ref.lse)
+    ref_out, ref_lse = oracle.attention(w, ref_sel)
+    _check_attention(_u16(fus.out), fus.lse.cpu().numpy(), ref_out, ref_lse, "fused bad pages")
+    assert err & q.QSA_DEVERR_PAGE_ID and err_ref & q.QSA_DEVERR_PAGE_ID
+
+
 def test_graph_capture_replay():
     """The three calls captured in one graph: every replay equals the eager step bitwise."""
     w = workload(ATT_SMALL[2])
