@@ -718,39 +718,44 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         }
         __syncthreads();
         if (scan_tmp[1] != (uint32_t)(S - 1)) return;
-        // the last split: every other partial's stores completed before its count; each wave
-        // takes the common max and the denominator over the splits, and its owned tile
-        float Ms = NEG_INF;
-        for (int sp = 0; sp < S; ++sp)
-            Ms = fmaxf(Ms, sp == s ? m_col
-                                   : __hip_atomic_load(tile_part + (int64_t)sp * PF + kOff + lane, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT));
+        // the last split: every partial's stores completed before its count. Each wave merges
+        // the partials (its owned tile, the denominators, the maxima) in ascending split order
+        // with a running max, eight splits at a time: a group's loads, its own partial's
+        // included, all issue before the first is used (clamped, unconditional), so a group
+        // costs one round trip. With at most eight splits this is one group and the plain
+        // weighted sum with the common max.
+        constexpr int kGroup = 8;
+        const int tsel = owns_tile ? wave : 0;
+        float Ms = NEG_INF, Ls = 0.0f;
         f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-        float Ls = 0.0f;
-        for (int sp = 0; sp < S; ++sp) {         // ascending split order
-            const float *part = tile_part + (int64_t)sp * PF;
-            f32x4 o;
-            float m, l;
-            if (sp == s) {
-                o = o_own;
-                m = m_col;
-                l = Lsum;
-            } else {
-                if (owns_tile) {
+        for (int sp0 = 0; sp0 < S; sp0 += kGroup) {
+            float mv[kGroup], lv[kGroup];
+            f32x4 ov[kGroup];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        o[i] = __hip_atomic_load(part + (wave * 4 + i) * 64 + lane, __ATOMIC_RELAXED,
+            for (int i = 0; i < kGroup; ++i) {
+                const float *part = tile_part + (int64_t)min(sp0 + i, S - 1) * PF;
+                mv[i] = __hip_atomic_load(part + kOff + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lv[i] = __hip_atomic_load(part + (NDT * 4) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ov[i][e] = __hip_atomic_load(part + (tsel * 4 + e) * 64 + lane, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
-                }
-                m = __hip_atomic_load(part + kOff + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                l = __hip_atomic_load(part + (NDT * 4) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            const float wgt = (m == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(m - Ms);
-            Ls = __builtin_fmaf(wgt, l, Ls);
-            if (owns_tile) {
+            float cm = Ms;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wgt, o[i], acc[i]);
+            for (int i = 0; i < kGroup; ++i)
+                if (sp0 + i < S) cm = fmaxf(cm, mv[i]);
+            const float resc = (Ms == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(Ms - cm);
+            Ls *= resc;
+            acc *= resc;
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                const float wgt = (sp0 + i >= S || mv[i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mv[i] - cm);
+                Ls = __builtin_fmaf(wgt, lv[i], Ls);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wgt, ov[i][e], acc[e]);
             }
+            Ms = cm;
         }
         o_own = acc;
         Lsum = Ls;
