@@ -78,7 +78,7 @@ int col_tiles(const qsa_shape *sh)
 
 // Splits per (request, KV head, column tile) when the caller leaves the choice to the
 // library: about one workgroup (8 waves) per CU over the 256 CUs, without splits so thin
-// that a wave gets less than one page of the expected union. (Two workgroups fit per CU;
+// that a wave gets less than half a page of the expected union. (Two workgroups fit per CU;
 // fewer, longer workgroups measured faster than one full round of short ones, because each
 // workgroup pays the union build and each split adds partials to merge.)
 int auto_splits(const qsa_shape *sh)
@@ -89,7 +89,7 @@ int auto_splits(const qsa_shape *sh)
     const int64_t rows_per_tile = std::max<int64_t>(1, std::min<int64_t>(sh->max_rows_per_request, tile_cols(sh) / G));
     const int64_t union_est = std::min<int64_t>(rows_per_tile * (sh->topk + sh->window), sh->max_pages);
     int64_t s = (kCUs + base - 1) / base;
-    const int64_t cap = std::max<int64_t>(1, union_est / kDecodeWaves);
+    const int64_t cap = std::max<int64_t>(1, 2 * union_est / kDecodeWaves);
     s = std::min(s, cap);
     s = std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplits));
     return (int)s;
