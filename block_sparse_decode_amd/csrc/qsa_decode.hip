@@ -13,10 +13,10 @@
 // splitting a tile's pages instead costs a merge.
 //  1. The tile's rows (at most 4 causal rows: verify rows, or a run of a context step's
 //     rows) each list their selected pages (computed here from the scores, one wave per
-//     row, when the selection is fused in). Wave 0
-//     builds the union of those pages, each with a row bitmask, in LDS, and drops entries
-//     whose page-table entry is -1. Each page of the union is read once for all the
-//     tile's rows.
+//     row, when the selection is fused in). Wave 0 builds the union of those pages, each
+//     with a row bitmask, in LDS, and drops entries whose page-table entry is -1. Each page
+//     of the union is read once for all the tile's rows. A one-row tile with the selection
+//     fused in has its selecting wave write the union directly.
 //  2. The union's 32-token sub-chunks are numbered page-major. Split s takes a contiguous
 //     range of them and its waves deal that range round-robin, so waves differ by at most
 //     one sub-chunk. Each wave runs an online softmax over its sub-chunks:
@@ -26,11 +26,13 @@
 //                      S^T accumulators, so P never leaves registers)
 //     Each lane's column masks tokens past its row's length (causal verify rows) and pages
 //     its row did not select.
-//  3. The waves merge in LDS in a fixed order. With one split the workgroup writes the
-//     final bf16 output and the LSE (the lean one-split form). Otherwise it writes its
-//     partial and bumps the tile's counter; the tile's last split to finish merges all S
-//     partials in ascending split order (so the result does not depend on which split is
-//     last), writes the output and puts the counter back to zero for the next call.
+//  3. The waves merge in a fixed order: each wave publishes the output tiles the others
+//     own, and after one barrier wave w sums output tile w over the waves. With one split
+//     the workgroup writes the final bf16 output and the LSE (the lean one-split form).
+//     Otherwise it writes its partial and bumps the tile's counter; the tile's last split to
+//     finish merges all S partials in ascending split order (so the result does not depend
+//     on which split is last), writes the output and puts the counter back to zero for the
+//     next call.
 // Workgroups are dispatched round-robin over the 8 XCDs by linear id; the id -> (tile,
 // split) map gives each XCD a contiguous run of (request, KV head, column tile, split)
 // items, so a tile's splits, and the tiles of one request and KV head (whose rows share
@@ -288,8 +290,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     // builds the union: each listed page ORs its row into the bitmap and bids its entry
     // index for the page's owner word (the smallest bid wins), and each page's owner
     // appends it, with ballot counts for the positions, so no workgroup barrier is needed.
-    // Meanwhile the last wave converts q into the MFMA B operand in LDS. Union order: by
-    // first listing (rows in order), a function of the input alone.
+    // The last wave converts q into the MFMA B operand in LDS before the first barrier. Union
+    // order: by first listing (rows in order), a function of the input alone.
     // A one-row tile with the selection fused in takes a shorter way: its selecting wave
     // holds the page-table entries of its columns in registers beside the score keys and
     // writes the union itself (the selected pages with a valid physical page, ascending, as
