@@ -144,6 +144,40 @@ def test_selection_on_injected_tie_heavy_scores(seed, MP, k, W, R):
     assert np.array_equal(sel.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("rows,context,k,W,splits", [(1, (64, 4000), 4, 1, 1), (1, (64, 4000), 0, 2, 1),
+                                                      (1, (100, 40000), 40, 3, 1), (2, (64, 9000), 6, 2, 2),
+                                                      (1, (3000, 60000), 200, 2, 2)])
+def test_fused_selection_on_injected_tie_heavy_scores(rows, context, k, W, splits):
+    """The selection fused into the attention launch (one-row tiles write their union from the
+    selecting wave) on scores from a 5-value set with NaN and -inf mixed in, k = 0 and k above
+    the candidates: the oracle's rows, and bit for bit the composed calls' outputs."""
+    cfg = synth.Config("fused_ties", 5, rows, 8, 2, 64, 64, context, k, W, seed=311 + k, invalid_frac=0.05)
+    w = workload(cfg)
+    b = DeviceBatch.upload(w)
+    rng = np.random.default_rng(17 + k)
+    vals = np.array([1.5, 0.0, -0.0, -2.0, 7.25], np.float32)
+    scores = vals[rng.integers(0, 5, size=(w.N, w.MP))]
+    holes = rng.random((w.N, w.MP))
+    scores[holes < 0.05] = np.nan
+    scores[(holes >= 0.05) & (holes < 0.1)] = -np.inf
+    print(f"[fused ties] rows={rows} MP={w.MP} k={k} W={W} splits={splits}", flush=True)
+    ref = Step(b, num_splits=splits, fused=False)
+    fus = Step(b, num_splits=splits, fused=True)
+    for st in (ref, fus):
+        st.scores.copy_(torch.from_numpy(scores).cuda())
+    ref.select_call()
+    ref.decode_call()
+    fus.selected.fill_(-7)
+    fus.select_decode_call()
+    torch.cuda.synchronize()
+    ref_sel = oracle.select_w(w, scores)
+    assert np.array_equal(ref.selected.cpu().numpy(), ref_sel)
+    assert np.array_equal(fus.selected.cpu().numpy(), ref_sel)
+    assert torch.equal(fus.out, ref.out) and torch.equal(fus.lse, ref.lse)
+    ref_out, ref_lse = oracle.attention(w, ref_sel)
+    _check_attention(_u16(fus.out), fus.lse.cpu().numpy(), ref_out, ref_lse, "fused ties")
+
+
 def test_selection_repeated_launch_determinism():
     """The same rows launched 50 times select identical sets in identical order."""
     w = workload("mtp_verify_32k")
