@@ -236,6 +236,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     constexpr float kLazy = 8.0f;
     static_assert(NDT * 64 * 16 <= 32 * D * 2, "a wave's published tiles must fit its V staging tile");
     static_assert(NDT <= NW, "every output tile needs an owner wave");
+    static_assert(SELC <= 32, "a one-row tile's selection mask is kept in 32 bits");
     static_assert(D / 8 <= 16, "one V row holds at most 16 swizzled chunks");
 
     // One LDS area: the union build's scratch (row-mask bitmap, page-table row, owner of each
