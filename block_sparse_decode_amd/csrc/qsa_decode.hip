@@ -221,8 +221,8 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
     return r;
 }
 
-// SELC = 0: the rows' selections are an input. SELC = 8 or 16: they are computed here from
-// the scores (select_row with that many columns per lane) and also written out.
+// SELC = 0: the rows' selections are an input. SELC = 2, 4, 8 or 16: they are computed here
+// from the scores (select_row with that many columns per lane) and also written out.
 template <int D, int SELC, int F>
 __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(DecodeParams prm)
 {
@@ -808,7 +808,11 @@ hipError_t launch_sparse_decode(const DecodeParams &prm, int D, hipStream_t stre
 
 hipError_t launch_select_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream)
 {
+    // columns per lane of the selection: the fewest that cover the table (fewer compares and
+    // popcounts per step of the bit search)
     if (prm.MP > 1024) return hipErrorInvalidValue;
+    if (prm.MP <= 128) return D == 64 ? launch_decode_d<64, 2>(prm, stream) : launch_decode_d<128, 2>(prm, stream);
+    if (prm.MP <= 256) return D == 64 ? launch_decode_d<64, 4>(prm, stream) : launch_decode_d<128, 4>(prm, stream);
     if (prm.MP <= 512) return D == 64 ? launch_decode_d<64, 8>(prm, stream) : launch_decode_d<128, 8>(prm, stream);
     return D == 64 ? launch_decode_d<64, 16>(prm, stream) : launch_decode_d<128, 16>(prm, stream);
 }

@@ -25,7 +25,11 @@ __global__ __launch_bounds__(64) void select_topk_kernel(SelectParams prm)
 hipError_t launch_select_topk(const SelectParams &prm, int B, hipStream_t stream)
 {
     dim3 grid(prm.rmax, B);
-    if (prm.MP <= 512)
+    if (prm.MP <= 128)
+        select_topk_kernel<2><<<grid, 64, 0, stream>>>(prm);
+    else if (prm.MP <= 256)
+        select_topk_kernel<4><<<grid, 64, 0, stream>>>(prm);
+    else if (prm.MP <= 512)
         select_topk_kernel<8><<<grid, 64, 0, stream>>>(prm);
     else if (prm.MP <= 1024)
         select_topk_kernel<16><<<grid, 64, 0, stream>>>(prm);

@@ -26,20 +26,21 @@
 namespace qsa {
 
 // Keys of the whole wave at or above t (wave-uniform): one ballot per register slot, all
-// compares of a group of 8 slots issued before the first scalar popcount reads a mask, so
-// their vector-to-scalar latencies overlap instead of adding up.
+// compares of a group of (up to) 8 slots issued before the first scalar popcount reads a mask,
+// so their vector-to-scalar latencies overlap instead of adding up.
 template <int C>
 __device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[C], uint32_t t)
 {
+    constexpr int GN = C < 8 ? C : 8;     // slots per group
     uint32_t c = 0;
 #pragma unroll
-    for (int g = 0; g < C; g += 8) {
-        uint64_t m[8];
+    for (int g = 0; g < C; g += GN) {
+        uint64_t m[GN];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m[i] = __ballot(key[g + i] >= t);
+        for (int i = 0; i < GN; ++i) m[i] = __ballot(key[g + i] >= t);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c += (uint32_t)__builtin_popcountll(m[i]);
+        for (int i = 0; i < GN; ++i) c += (uint32_t)__builtin_popcountll(m[i]);
     }
     return c;
 }
