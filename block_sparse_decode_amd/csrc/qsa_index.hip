@@ -25,6 +25,7 @@
 namespace qsa {
 
 constexpr int kIndexWaves = 4;
+constexpr int kIndexCUs = 256;
 constexpr int kHeadGroup = 8;        // q heads per pass
 
 // acc[t] = fma(q_t[16c + n], k[16c + n], acc[t]) for n = 0 .. 15 in order and t = 0 .. 7:
@@ -50,10 +51,12 @@ __device__ __forceinline__ void fmac16x8(float (&a)[kHeadGroup], const float (&q
 #undef QSA_FMAC8
 #undef QSA_FMAC
 
-template <int D>
-__global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(IndexParams prm)
+// NW waves per workgroup, each taking KV heads wave, wave + NW, ...: 4 by default; 8 when the
+// grid is small and there are at least 8 KV heads, so that the KV heads of a (row, page tile)
+// spread over more SIMDs.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams prm)
 {
-    constexpr int NW = kIndexWaves;
     constexpr int HG = kHeadGroup;
     __shared__ float red[NW][kWave];
     constexpr int NC = D / 16;                        // 16-element chunks of a row
@@ -192,10 +195,17 @@ __global__ __launch_bounds__(kIndexWaves * 64, 2) void index_scores_kernel(Index
 hipError_t launch_index_scores(const IndexParams &prm, int D, int B, hipStream_t stream)
 {
     dim3 grid((prm.MP + kWave - 1) / kWave, prm.rmax, B);
-    if (D == 64)
-        index_scores_kernel<64><<<grid, 256, 0, stream>>>(prm);
-    else
-        index_scores_kernel<128><<<grid, 256, 0, stream>>>(prm);
+    // a grid of fewer waves than two per SIMD (4 x 256) takes eight waves per workgroup when
+    // the KV heads are enough to occupy them
+    const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+    const bool wide = prm.Hkv >= 8 && wgs * kIndexWaves < 2 * 4 * kIndexCUs;
+    if (D == 64) {
+        if (wide) index_scores_kernel<64, 8><<<grid, 512, 0, stream>>>(prm);
+        else index_scores_kernel<64, kIndexWaves><<<grid, kIndexWaves * 64, 0, stream>>>(prm);
+    } else {
+        if (wide) index_scores_kernel<128, 8><<<grid, 512, 0, stream>>>(prm);
+        else index_scores_kernel<128, kIndexWaves><<<grid, kIndexWaves * 64, 0, stream>>>(prm);
+    }
     return hipGetLastError();
 }
 
