@@ -53,14 +53,18 @@ __device__ __forceinline__ void fmac16x8(float (&a)[kHeadGroup], const float (&q
 
 // NW waves per workgroup, each taking KV heads wave, wave + NW, ...: 4 by default; 8 when the
 // grid is small and there are at least 8 KV heads, so that the KV heads of a (row, page tile)
-// spread over more SIMDs.
-template <int D, int NW>
+// spread over more SIMDs. ONEG: at most 8 q heads per KV head, so one pass covers them all and
+// the key is converted to fp32 one 16-element chunk at a time instead of being kept whole;
+// that halves the VGPRs, and a large grid then holds four waves per SIMD instead of two, so
+// one wave's loads overlap another's fmas.
+template <int D, int NW, bool ONEG>
 __global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams prm)
 {
     constexpr int HG = kHeadGroup;
     __shared__ float red[NW][kWave];
     constexpr int NC = D / 16;                        // 16-element chunks of a row
-    // per wave: q of one head group, [head][element mod 16][element / 16]
+    // per wave: q of one head group, [head][element mod 16][element / 16]; with ONEG
+    // [element / 16][element mod 16][head], so that a chunk's eight heads are adjacent
     __shared__ __align__(16) float qs[NW][HG][16][NC];
 
     const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -129,6 +133,50 @@ __global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams pr
             if (t < nh && !(a[t] != a[t]) && ((best != best) || a[t] > best)) best = a[t];
     };
 
+    if constexpr (ONEG) {
+        float *qf = &qs[wv][0][0][0];
+        for (int g = wv; g < prm.Hkv && any_cand; g += NW) {
+            uint32_t qu[HG];
+            load_q(g, 0, qu);
+            const uint4 *kp = reinterpret_cast<const uint4 *>(prm.keys + ((int64_t)(cand ? phys : 0) * prm.Hkv + g) * D);
+            uint4 kraw[D / 8];
+#pragma unroll
+            for (int c = 0; c < D / 8; ++c) kraw[c] = kp[c];
+            __builtin_amdgcn_sched_barrier(0);    // keep every key load ahead of the wait for q
+            // q as fp32: element e of head t at [(e / 16) * 16 + e % 16][t]
+            if (lane < D / 2) {
+                float4 *dst = reinterpret_cast<float4 *>(qf + 2 * lane * HG);
+                dst[0] = make_float4(bf16lo(qu[0]), bf16lo(qu[1]), bf16lo(qu[2]), bf16lo(qu[3]));
+                dst[1] = make_float4(bf16lo(qu[4]), bf16lo(qu[5]), bf16lo(qu[6]), bf16lo(qu[7]));
+                dst[2] = make_float4(bf16hi(qu[0]), bf16hi(qu[1]), bf16hi(qu[2]), bf16hi(qu[3]));
+                dst[3] = make_float4(bf16hi(qu[4]), bf16hi(qu[5]), bf16hi(qu[6]), bf16hi(qu[7]));
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): this wave's q is in LDS
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float a[HG];
+#pragma unroll
+            for (int t = 0; t < HG; ++t) a[t] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                // chunk c of q: head t's element 16c + m in lane m of each 16-lane row
+                const float4 *src = reinterpret_cast<const float4 *>(qf + (c * 16 + (lane & 15)) * HG);
+                const float4 q0 = src[0], q1 = src[1];
+                const float qc[HG] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                float kk[16];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint4 v = kraw[2 * c + h];
+                    float *k8 = &kk[8 * h];
+                    k8[0] = bf16lo(v.x); k8[1] = bf16hi(v.x); k8[2] = bf16lo(v.y); k8[3] = bf16hi(v.y);
+                    k8[4] = bf16lo(v.z); k8[5] = bf16hi(v.z); k8[6] = bf16lo(v.w); k8[7] = bf16hi(v.w);
+                }
+                fmac16x8(a, qc, kk);
+            }
+            fold(a, G);
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next KV head's staging
+        }
+    } else
     for (int g = wv; g < prm.Hkv && any_cand; g += NW) {
         // q of the first head group, then this page's key for KV head g: every load is issued
         // before the first wait, and the q loads first, so waiting for q leaves the key loads
@@ -199,12 +247,24 @@ hipError_t launch_index_scores(const IndexParams &prm, int D, int B, hipStream_t
     // the KV heads are enough to occupy them
     const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
     const bool wide = prm.Hkv >= 8 && wgs * kIndexWaves < 2 * 4 * kIndexCUs;
+    const bool oneg = prm.Hq <= kHeadGroup * prm.Hkv;
+    auto go = [&](auto kern, int nw) { kern<<<grid, nw * 64, 0, stream>>>(prm); };
     if (D == 64) {
-        if (wide) index_scores_kernel<64, 8><<<grid, 512, 0, stream>>>(prm);
-        else index_scores_kernel<64, kIndexWaves><<<grid, kIndexWaves * 64, 0, stream>>>(prm);
+        if (oneg) {
+            if (wide) go(index_scores_kernel<64, 8, true>, 8);
+            else go(index_scores_kernel<64, kIndexWaves, true>, kIndexWaves);
+        } else {
+            if (wide) go(index_scores_kernel<64, 8, false>, 8);
+            else go(index_scores_kernel<64, kIndexWaves, false>, kIndexWaves);
+        }
     } else {
-        if (wide) index_scores_kernel<128, 8><<<grid, 512, 0, stream>>>(prm);
-        else index_scores_kernel<128, kIndexWaves><<<grid, kIndexWaves * 64, 0, stream>>>(prm);
+        if (oneg) {
+            if (wide) go(index_scores_kernel<128, 8, true>, 8);
+            else go(index_scores_kernel<128, kIndexWaves, true>, kIndexWaves);
+        } else {
+            if (wide) go(index_scores_kernel<128, 8, false>, 8);
+            else go(index_scores_kernel<128, kIndexWaves, false>, kIndexWaves);
+        }
     }
     return hipGetLastError();
 }
