@@ -99,6 +99,11 @@ SMALL = [
     synth.Config("s_verify_ragged", 5, 4, 16, 2, 128, 64, (60, 3000), 6, 2, seed=102, invalid_frac=0.1),
     synth.Config("s_hkv8_p128", 3, 2, 16, 8, 128, 128, (500, 9000), 8, 1, seed=103, max_pages=77),
     synth.Config("s_g1_d64", 2, 3, 4, 4, 64, 128, (129, 700), 3, 3, seed=104, dup_key_frac=0.3),
+    # more than 8 q heads per KV head: several head groups per KV head, the last one partial
+    # at 12, and at 8 KV heads on a small grid the eight-wave launch
+    synth.Config("s_g16_d128", 2, 4, 32, 2, 128, 64, 9000, 6, 2, seed=105),
+    synth.Config("s_g12_d64", 2, 2, 24, 2, 64, 64, (100, 3000), 5, 1, seed=106, dup_key_frac=0.2),
+    synth.Config("s_hkv8_g12", 2, 1, 96, 8, 128, 64, (200, 2000), 4, 1, seed=107, invalid_frac=0.05),
 ]
 CONFIG_NAMES = list(synth.CONFIGS)
 
