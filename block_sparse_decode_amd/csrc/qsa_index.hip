@@ -8,9 +8,10 @@
 // Design for gfx950. This stage feeds an exact integer decision (the top-k), so its fp32
 // arithmetic must be reproducible bit for bit. It therefore runs on the plain ALUs, never
 // on MFMA, whose internal summation order is not specified. A workgroup covers 64 pages of
-// one query row; each lane owns one page and keeps that page's key for the current KV head
-// in VGPRs as fp32. Each wave takes KV heads in turn, eight of the KV head's q heads per
-// pass. q is wave-uniform, so it reaches the lanes through the cross-lane operand network
+// one query row; each lane owns one page and holds that page's key for the current KV head
+// in VGPRs: as raw bf16 pairs, converted to fp32 one 16-element chunk at a time when one pass
+// covers all of the KV head's q heads (at most 8), else kept whole as fp32 for the later
+// passes. Each wave takes KV heads in turn, eight of the KV head's q heads per pass. q is wave-uniform, so it reaches the lanes through the cross-lane operand network
 // rather than through per-element LDS reads: a VGPR holds 16 consecutive elements of one
 // head, element m in lane m of every 16-lane row, and each v_fmac_f32 reads its q operand
 // through DPP row_newbcast, which hands one lane's value to its whole row. Each head's sum
