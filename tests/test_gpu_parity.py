@@ -104,6 +104,8 @@ SMALL = [
     synth.Config("s_g16_d128", 2, 4, 32, 2, 128, 64, 9000, 6, 2, seed=105),
     synth.Config("s_g12_d64", 2, 2, 24, 2, 64, 64, (100, 3000), 5, 1, seed=106, dup_key_frac=0.2),
     synth.Config("s_hkv8_g12", 2, 1, 96, 8, 128, 64, (200, 2000), 4, 1, seed=107, invalid_frac=0.05),
+    # a large grid (6400 waves) with an odd number of rows per request
+    synth.Config("s_rows5_large", 64, 5, 16, 2, 64, 64, (3000, 20000), 8, 1, seed=108, invalid_frac=0.05),
 ]
 CONFIG_NAMES = list(synth.CONFIGS)
 
