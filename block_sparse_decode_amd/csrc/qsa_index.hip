@@ -248,6 +248,7 @@ hipError_t launch_index_scores(const IndexParams &prm, int D, int B, hipStream_t
     // the KV heads are enough to occupy them
     const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
     const bool wide = prm.Hkv >= 8 && wgs * kIndexWaves < 2 * 4 * kIndexCUs;
+    // at most 8 q heads per KV head: one pass per KV head, the key converted chunk by chunk
     const bool oneg = prm.Hq <= kHeadGroup * prm.Hkv;
     auto go = [&](auto kern, int nw) { kern<<<grid, nw * 64, 0, stream>>>(prm); };
     if (D == 64) {
