@@ -158,11 +158,18 @@ __global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams pr
             float a[HG];
 #pragma unroll
             for (int t = 0; t < HG; ++t) a[t] = 0.0f;
+            // chunk c of q: head t's element 16c + m in lane m of each 16-lane row; the next
+            // chunk's reads are issued before this chunk's fmas, so their latency is hidden
+            const float4 *qsrc = reinterpret_cast<const float4 *>(qf + (lane & 15) * HG);
+            float4 q0n = qsrc[0], q1n = qsrc[1];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                // chunk c of q: head t's element 16c + m in lane m of each 16-lane row
-                const float4 *src = reinterpret_cast<const float4 *>(qf + (c * 16 + (lane & 15)) * HG);
-                const float4 q0 = src[0], q1 = src[1];
+                const float4 q0 = q0n, q1 = q1n;
+                if (c + 1 < NC) {
+                    q0n = qsrc[(c + 1) * 16 * HG / 4];
+                    q1n = qsrc[(c + 1) * 16 * HG / 4 + 1];
+                }
+                __builtin_amdgcn_sched_barrier(0);    // the next chunk's reads stay ahead of these fmas
                 const float qc[HG] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
                 float kk[16];
 #pragma unroll
