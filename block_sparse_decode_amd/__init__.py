@@ -20,7 +20,7 @@ __all__ = [
     "Plane", "qsa_rollback_stash_bytes", "qsa_rollback_gather", "qsa_rollback_restore", "qsa_step_slots",
     "QSA_DEVERR_SLOT",
     "QSA_DEVERR_PAGE_ID", "QSA_DEVERR_SEQ_LEN", "QSA_DEVERR_ROWS", "QSA_DEVERR_Q_RANGE",
-    "QSA_DEVERR_SELECTED",
+    "QSA_DEVERR_SELECTED", "DecodePlan", "qsa_plan_decode",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +40,7 @@ QSA_MAX_PLANES = 16
 EXPORTED = (
     "qsa_index_scores", "qsa_select_topk", "qsa_workspace_bytes", "qsa_sparse_decode", "qsa_select_sparse_decode",
     "qsa_kv_store", "qsa_rollback_stash_bytes", "qsa_step_slots", "qsa_rollback_gather", "qsa_rollback_restore",
-    "qsa_nvfp4_dequant_pages", "qsa_status_string", "qsa_abi_version",
+    "qsa_nvfp4_dequant_pages", "qsa_status_string", "qsa_abi_version", "qsa_plan_decode",
 )
 
 
@@ -87,6 +87,20 @@ class Paged(ctypes.Structure):
     ]
 
 
+class DecodePlan(ctypes.Structure):
+    """Mirror of `qsa_decode_plan`: the launch the attention calls make for a shape."""
+    _fields_ = [
+        ("tile_cols", ctypes.c_int32),
+        ("rows_per_tile", ctypes.c_int32),
+        ("col_tiles", ctypes.c_int32),
+        ("splits", ctypes.c_int32),
+        ("select_cols", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("workgroups", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class Plane(ctypes.Structure):
     """Mirror of `qsa_plane`: one plane of the rollback (a device byte array and the strides
     that address row r of it: base + pages[r] * page_stride + within[r] * slot_stride +
@@ -122,6 +136,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_select_topk.argtypes = [sp, pp, P, P, P]
         L.qsa_workspace_bytes.argtypes = [sp, I32]
         L.qsa_workspace_bytes.restype = SZ
+        L.qsa_plan_decode.argtypes = [sp, I32, I32, ctypes.POINTER(DecodePlan)]
         L.qsa_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, I32, P, SZ, P]
         L.qsa_select_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, P, I32, P, SZ, P]
         L.qsa_kv_store.argtypes = [sp, pp, P, P, P]
@@ -137,7 +152,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_abi_version.restype = I32
         for name in ("qsa_index_scores", "qsa_select_topk", "qsa_sparse_decode", "qsa_select_sparse_decode",
                      "qsa_kv_store", "qsa_nvfp4_dequant_pages", "qsa_rollback_gather", "qsa_rollback_restore",
-                     "qsa_step_slots"):
+                     "qsa_step_slots", "qsa_plan_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -185,6 +200,13 @@ def qsa_select_topk(shape: Shape, paged: Paged, scores, selected, stream=None) -
 
 def qsa_workspace_bytes(shape: Shape, num_splits: int = 0) -> int:
     return int(lib().qsa_workspace_bytes(ctypes.byref(shape), int(num_splits)))
+
+
+def qsa_plan_decode(shape: Shape, num_splits: int = 0, fused: bool = True) -> DecodePlan:
+    plan = DecodePlan()
+    _check(lib().qsa_plan_decode(ctypes.byref(shape), int(num_splits), int(bool(fused)), ctypes.byref(plan)),
+           "qsa_plan_decode")
+    return plan
 
 
 def qsa_sparse_decode(shape: Shape, paged: Paged, q, selected, out, lse=None, num_splits: int = 0,

@@ -18,6 +18,8 @@ constexpr int kTileMaxRows = 4;      // rows per attention tile (row-mask byte, 
 constexpr int kMaxPages = 4096;
 constexpr int kMaxKW = 256;
 constexpr int kMaxSplits = 64;
+constexpr int64_t kCounterSlots = 8192;                 // split tiles per call
+constexpr size_t kCounterBytes = kCounterSlots * sizeof(uint32_t);
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -95,30 +97,30 @@ int auto_splits(const qsa_shape *sh)
     return (int)s;
 }
 
-int resolve_splits(const qsa_shape *sh, int32_t num_splits)
-{
-    if (num_splits <= 0) return auto_splits(sh);
-    return num_splits > kMaxSplits ? kMaxSplits : num_splits;
-}
-
 int64_t decode_tiles(const qsa_shape *sh)
 {
     return (int64_t)sh->num_requests * sh->num_kv_heads * col_tiles(sh);
 }
 
-// Workspace of a split decode: one counter per tile first (so that their place does not
-// depend on the split count and a workspace can serve calls with different counts), then
-// the partials of every (tile, split).
-size_t decode_counter_bytes(const qsa_shape *sh)
+// Splits per tile: the caller's count (clamped to kMaxSplits) or the library's choice. A split
+// tile needs a completion counter, and the counters live in a region of fixed size at the
+// start of the workspace (kCounterSlots words), so a batch with more tiles than that runs one
+// split per tile. Splitting pays only when tiles are fewer than CUs, so the automatic choice
+// never reaches that bound.
+int resolve_splits(const qsa_shape *sh, int32_t num_splits)
 {
-    return ((size_t)decode_tiles(sh) * sizeof(uint32_t) + 255) & ~(size_t)255;
+    const int s = num_splits <= 0 ? auto_splits(sh) : (num_splits > kMaxSplits ? kMaxSplits : num_splits);
+    return decode_tiles(sh) > kCounterSlots ? 1 : s;
 }
 
+// Workspace of a split decode: the counter region first, at a fixed size that does not depend
+// on the shape, then the partials of every (tile, split). A workspace therefore keeps its
+// counters where every later call looks for them, whatever that call's batch or split count,
+// and no call's partials ever overlap a counter.
 size_t decode_ws_bytes(const qsa_shape *sh, int splits)
 {
     if (splits <= 1) return 0;
-    return decode_counter_bytes(sh) +
-           (size_t)decode_tiles(sh) * splits * decode_part_floats(sh->head_dim) * sizeof(float);
+    return kCounterBytes + (size_t)decode_tiles(sh) * splits * decode_part_floats(sh->head_dim) * sizeof(float);
 }
 
 }  // namespace
@@ -202,6 +204,24 @@ size_t qsa_workspace_bytes(const qsa_shape *sh, int32_t num_splits)
     return decode_ws_bytes(sh, resolve_splits(sh, num_splits));
 }
 
+qsa_status qsa_plan_decode(const qsa_shape *sh, int32_t num_splits, int32_t fused, qsa_decode_plan *plan)
+{
+    const qsa_status st = check_shape(sh);
+    if (st != QSA_OK) return st;
+    if (!plan || num_splits < 0) return QSA_ERR_INVALID_ARG;
+    const int G = sh->num_q_heads / sh->num_kv_heads;
+    const int splits = resolve_splits(sh, num_splits);
+    plan->tile_cols = tile_cols(sh);
+    plan->rows_per_tile = G <= 16 ? plan->tile_cols / G : 0;
+    plan->col_tiles = col_tiles(sh);
+    plan->splits = splits;
+    plan->select_cols = (fused && sh->topk + sh->window > 0) ? fused_select_cols(sh->max_pages) : 0;
+    const int64_t items = decode_tiles(sh) * splits;
+    plan->workgroups = (items + kXcdCount - 1) / kXcdCount * kXcdCount;
+    plan->workspace_bytes = decode_ws_bytes(sh, splits);
+    return QSA_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -253,7 +273,7 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     prm.out = out;
     prm.lse = lse;
     prm.counters = need ? reinterpret_cast<uint32_t *>(workspace) : nullptr;
-    prm.part = need ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + decode_counter_bytes(sh))
+    prm.part = need ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kCounterBytes)
                     : nullptr;
     prm.err = pg->error_word;
     prm.NP = sh->num_phys_pages;

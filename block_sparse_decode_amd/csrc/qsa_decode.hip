@@ -48,7 +48,7 @@ namespace qsa {
 
 constexpr int kMaxUnion = 1024;     // rows (<= 4) x (k + W) (<= 256)
 constexpr int kMaxPages = 4096;     // page-table stride MP
-constexpr int kXcds = 8;
+constexpr int kXcds = kXcdCount;
 
 __device__ __forceinline__ void wave_lds_fence()
 {
@@ -808,13 +808,13 @@ hipError_t launch_sparse_decode(const DecodeParams &prm, int D, hipStream_t stre
 
 hipError_t launch_select_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream)
 {
-    // columns per lane of the selection: the fewest that cover the table (fewer compares and
-    // popcounts per step of the bit search)
-    if (prm.MP > 1024) return hipErrorInvalidValue;
-    if (prm.MP <= 128) return D == 64 ? launch_decode_d<64, 2>(prm, stream) : launch_decode_d<128, 2>(prm, stream);
-    if (prm.MP <= 256) return D == 64 ? launch_decode_d<64, 4>(prm, stream) : launch_decode_d<128, 4>(prm, stream);
-    if (prm.MP <= 512) return D == 64 ? launch_decode_d<64, 8>(prm, stream) : launch_decode_d<128, 8>(prm, stream);
-    return D == 64 ? launch_decode_d<64, 16>(prm, stream) : launch_decode_d<128, 16>(prm, stream);
+    switch (fused_select_cols(prm.MP)) {
+    case 2: return D == 64 ? launch_decode_d<64, 2>(prm, stream) : launch_decode_d<128, 2>(prm, stream);
+    case 4: return D == 64 ? launch_decode_d<64, 4>(prm, stream) : launch_decode_d<128, 4>(prm, stream);
+    case 8: return D == 64 ? launch_decode_d<64, 8>(prm, stream) : launch_decode_d<128, 8>(prm, stream);
+    case 16: return D == 64 ? launch_decode_d<64, 16>(prm, stream) : launch_decode_d<128, 16>(prm, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 // ---- parity hook: whole pages through the same decode as the attention kernel ----------

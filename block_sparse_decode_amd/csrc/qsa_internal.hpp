@@ -158,6 +158,15 @@ hipError_t launch_step_slots(const SlotParams &prm, int B, hipStream_t stream);
 // number of waves per decode workgroup
 constexpr int kDecodeWaves = 8;
 
+// XCDs of the chip; decode workgroups are numbered so that each XCD takes a contiguous run of
+// work items (the grid is rounded up to a multiple of this)
+constexpr int kXcdCount = 8;
+
+// Score columns per lane of the selection fused into the attention launch: the fewest that
+// cover the table (each bit-search step costs a compare and a popcount per column); 0 when
+// the table is too wide and the launch runs the separate selection kernel first.
+constexpr int fused_select_cols(int MP) { return MP <= 128 ? 2 : MP <= 256 ? 4 : MP <= 512 ? 8 : MP <= 1024 ? 16 : 0; }
+
 // A split's partial result for one tile (16 query columns): the unnormalised O^T
 // accumulators of the d/16 output tiles and the ones tile (the softmax denominator), laid
 // out [tile][element 0..3][lane], then the column max (log2 units) per lane.

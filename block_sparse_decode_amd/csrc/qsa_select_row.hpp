@@ -1,9 +1,10 @@
 // qsa_select_row.hpp -- canonical top-k plus window of one query row, by one wave.
 //
-// Method: TensorRT-LLM PR #20276, Features, "Canonical QSA selection" (the selection row is a
-// pure function of the scores, the window and k: every block strictly above the k-th score,
-// ties to the highest index) and Decisions worth knowing (the result must not follow launch
-// order). Shared by the select kernel and the attention kernel's fused selection.
+// Method: TensorRT-LLM PR #20276, Features, "Canonical QSA selection" row, and Decisions worth
+// knowing. The rule: a row's selection depends on its scores, W and k alone. Candidates whose
+// score exceeds the k-th largest are kept; among candidates equal to that value, the larger
+// page index is ranked first; and no launch order may change the result. Shared by the select
+// kernel and the attention kernel's fused selection.
 //
 // One wave, no LDS, no barrier. Lane l holds columns l*C .. l*C + C - 1 (C >= MP/64) as
 // order-preserving uint32 keys in registers, so lane-major order is ascending page order.

@@ -132,9 +132,9 @@ qsa_status qsa_index_scores(const qsa_shape *shape, const qsa_paged *paged,
 
 /*
  * Canonical top-k selection plus local window (PR #20276, Features, "Canonical QSA
- * selection": the selection row is a pure function of the scores, the window and k,
- * taking every block strictly above the k-th score with ties to the highest index;
- * Decisions worth knowing: the result must not depend on launch order).
+ * selection" row, and Decisions worth knowing). A row's result depends on its scores, W and
+ * k only: candidates scoring above the k-th largest value are kept, equal scores are ranked
+ * by descending page index, and the launch order never changes the result.
  *   scores    fp32  [N][MP]     (device)
  *   selected  int32 [N][k + W]  (device, written in full)
  * Per row (n as above): the window is pages [max(0, n - W), n). Candidates are columns
@@ -149,14 +149,45 @@ qsa_status qsa_select_topk(const qsa_shape *shape, const qsa_paged *paged,
 /*
  * Workspace needed by qsa_sparse_decode for `num_splits` (0 = the library's choice for
  * this shape). Returns 0 when the call needs none (one split). Also 0 for an invalid shape.
- * The workspace holds each split's partial result and one completion counter per
- * (request, KV head, 16-column tile). The counters must be zero when a call starts: fill
- * a new workspace with zeros once (e.g. hipMemsetAsync) before its first use. Every call
- * leaves them zero again, so a workspace can be reused by later calls, with any split
- * count, with no further clearing (also inside captured graphs). Two calls that may
- * overlap in time must not share a workspace.
+ * The workspace holds a region of completion counters of fixed size (32 KiB, one counter per
+ * split tile, at most 8192 tiles: a batch with more tiles runs one split per tile), then each
+ * split's partial result. The counters must be zero when a call starts: fill a new workspace
+ * with zeros once (e.g. hipMemsetAsync) before its first use. Every call leaves them zero
+ * again, and their place does not depend on the shape, so a workspace can be reused by later
+ * calls of any batch, shape or split count (as long as it is large enough) with no further
+ * clearing (also inside captured graphs). Two calls that may overlap in time must not share
+ * a workspace.
  */
 size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
+
+/*
+ * The launch the attention calls make for this shape (host only; nothing is launched).
+ * A tile is a run of at most 16 of one request's query columns (its rows x the G q heads of
+ * one KV head, row-major); every page any of its rows selected is read once for the tile
+ * (PR #20276, Performance > What runs on the fast paths: K/V tiles read once per group of
+ * rows). `fused` != 0 describes qsa_select_sparse_decode, 0 qsa_sparse_decode.
+ *   tile_cols       query columns per tile (1..16)
+ *   rows_per_tile   whole rows per tile (tile_cols / G) when G <= 16; 0 when tiles cut rows
+ *   col_tiles       tiles per (request, KV head)
+ *   splits          KV splits per tile (as qsa_sparse_decode resolves num_splits)
+ *   select_cols     score columns per lane of the fused selection (2, 4, 8 or 16), 0 when
+ *                   not fused or when max_pages > 1024 (a separate selection launch runs first)
+ *   workgroups      attention workgroups launched
+ *   workspace_bytes qsa_workspace_bytes(shape, num_splits)
+ * QSA_ERR_INVALID_ARG for a NULL plan, negative num_splits or an invalid shape.
+ */
+typedef struct qsa_decode_plan {
+    int32_t tile_cols;
+    int32_t rows_per_tile;
+    int32_t col_tiles;
+    int32_t splits;
+    int32_t select_cols;
+    int32_t reserved;
+    int64_t workgroups;
+    size_t  workspace_bytes;
+} qsa_decode_plan;
+
+qsa_status qsa_plan_decode(const qsa_shape *shape, int32_t num_splits, int32_t fused, qsa_decode_plan *plan);
 
 /*
  * Split-KV sparse GQA attention over the selected pages, with an LSE merge (PR #20937,

@@ -214,10 +214,10 @@ static int int_cmp(const void *a, const void *b)
     return (x > y) - (x < y);
 }
 
-/* Canonical QSA selection [PR20276, Features, "Canonical QSA selection": the
-   selection row is a pure function of the scores, the window and k, taking
-   every block strictly above the k-th score with ties going to the highest
-   index; Decisions worth knowing: radix launch order must not matter].
+/* Canonical QSA selection [PR20276, Features, "Canonical QSA selection" row;
+   Decisions worth knowing]. The result depends on the scores, W and k alone:
+   candidates scoring above the k-th largest value are kept, and among equal
+   scores the larger page index ranks first, whatever the launch order.
    For each row: window = pages [max(0, n - W), n). Candidates = columns
    p < n - W whose score is neither NaN nor -inf. Take the first min(k, |C|)
    candidates in canonical order, add the window, sort ascending, and pad with -1

@@ -282,19 +282,76 @@ def test_workspace_sizing():
     sh = _shape()
     assert q.qsa_workspace_bytes(sh, 1) == 0
     # 2 requests x 4 KV heads x 4 tiles: 4 rows x 8 q heads per KV head, one row per tile
-    # (grouping rows would leave fewer tiles than CUs); one uint32 counter per tile (padded
-    # to 256 bytes), then per (tile, split) 9 accumulator tiles (8 of d 128 + the
-    # denominator) of 64 lanes x 4 floats, plus 64 column maxima
+    # (grouping rows would leave fewer tiles than CUs); a fixed 32 KiB counter region, then
+    # per (tile, split) 9 accumulator tiles (8 of d 128 + the denominator) of 64 lanes x 4
+    # floats, plus 64 column maxima
     tiles = 2 * 4 * 4
     part = tiles * 4 * (9 * 64 * 4 + 64) * 4
-    assert q.qsa_workspace_bytes(sh, 4) == 256 + part
+    assert q.qsa_workspace_bytes(sh, 4) == 32768 + part
     assert q.qsa_workspace_bytes(sh, 1000) == q.qsa_workspace_bytes(sh, 64)
+    # the counter region does not grow with the batch: only the partials do
+    big = _shape(num_requests=200, num_rows=800)
+    tiles_big = 200 * 4 * 2                     # enough tiles for two rows per tile
+    assert q.qsa_workspace_bytes(big, 2) == 32768 + tiles_big * 2 * (9 * 64 * 4 + 64) * 4
+    # past 8192 tiles a split is not possible (no counter for it): one split, no workspace
+    huge = _shape(num_requests=1100, num_rows=4400)
+    assert 1100 * 4 * 2 > 8192 and q.qsa_workspace_bytes(huge, 4) == 0
     # a too-small workspace is refused before any launch
     pg = _paged()
     assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 4, FAKE,
                 q.qsa_workspace_bytes(sh, 4) - 1, None) == 3
     assert _rawd("qsa_sparse_decode", ctypes.byref(sh), ctypes.byref(pg), FAKE, FAKE, FAKE, None, 4, None,
                 1 << 30, None) == 3
+
+
+def test_plan_struct_layout(tmp_path):
+    prog = tmp_path / "plan.c"
+    prog.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "qsa.h"
+int main(void) {
+  printf("%zu %zu %zu %zu\n", sizeof(qsa_decode_plan), offsetof(qsa_decode_plan, select_cols),
+         offsetof(qsa_decode_plan, workgroups), offsetof(qsa_decode_plan, workspace_bytes));
+  return 0;
+}
+''')
+    exe = tmp_path / "plan"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
+    got = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()))
+    D = q.DecodePlan
+    assert got == [ctypes.sizeof(D), D.select_cols.offset, D.workgroups.offset, D.workspace_bytes.offset]
+
+
+@pytest.mark.parametrize("B,R,Hq,Hkv,MP,rows,cols,ctiles", [
+    (16, 4, 32, 4, 512, 1, 8, 4),      # the 32K verify workload: 256 one-row tiles
+    (32, 4, 32, 4, 64, 2, 16, 2),      # 2 rows x 8 q heads: 256 tiles
+    (64, 4, 16, 4, 64, 4, 16, 1),      # 4 rows x 4 q heads: 256 tiles
+    (64, 3, 20, 4, 64, 3, 15, 1),      # 3 rows x 5 q heads
+    (8, 4, 16, 4, 64, 1, 4, 4),        # few tiles: rows halved down to one
+    (8, 2, 48, 2, 64, 0, 16, 3),       # 24 q heads per KV head: tiles cut rows
+])
+def test_plan_tile_heights(B, R, Hq, Hkv, MP, rows, cols, ctiles):
+    sh = _shape(num_requests=B, num_rows=B * R, max_rows_per_request=R, num_q_heads=Hq, num_kv_heads=Hkv,
+                max_pages=MP)
+    p = q.qsa_plan_decode(sh, 0, True)
+    assert (p.rows_per_tile, p.tile_cols, p.col_tiles) == (rows, cols, ctiles)
+    assert p.workspace_bytes == q.qsa_workspace_bytes(sh, 0)
+    assert p.workgroups % 8 == 0 and p.workgroups >= B * Hkv * ctiles * p.splits
+    assert p.select_cols == (2 if MP <= 128 else 8)
+    assert q.qsa_plan_decode(sh, 0, False).select_cols == 0
+    assert q.qsa_plan_decode(sh, 3, True).splits == 3
+
+
+def test_plan_select_cols_and_validation():
+    for MP, c in ((16, 2), (128, 2), (129, 4), (256, 4), (512, 8), (1024, 16), (1025, 0), (4096, 0)):
+        assert q.qsa_plan_decode(_shape(max_pages=MP), 0, True).select_cols == c, MP
+    assert q.qsa_plan_decode(_shape(topk=0, window=0), 0, True).select_cols == 0
+    plan = q.DecodePlan()
+    assert _raw("qsa_plan_decode", ctypes.byref(_shape()), 0, 1, None) == 1
+    assert _raw("qsa_plan_decode", ctypes.byref(_shape()), -1, 1, ctypes.byref(plan)) == 1
+    assert _raw("qsa_plan_decode", ctypes.byref(_shape(head_dim=96)), 0, 1, ctypes.byref(plan)) == 2
+    assert _raw("qsa_plan_decode", None, 0, 1, ctypes.byref(plan)) == 1
 
 
 def test_empty_batches_are_no_ops():

@@ -294,6 +294,11 @@ def test_fused_select_decode_equals_composed(cfg, splits):
     assert torch.equal(fus.out, ref.out)
     assert torch.equal(fus.lse, ref.lse)
     assert int(b.error_word[0].item()) == 0
+    if not isinstance(cfg, str):
+        # the small and wide-table cases are also compared with the oracle on every output
+        # (the full-size workloads on sampled outputs, in test_attention_full_size_sampled)
+        ref_out, ref_lse = oracle.attention(w, ref_sel)
+        _check_attention(_u16(fus.out), fus.lse.cpu().numpy(), ref_out, ref_lse, w.cfg.name)
 
 
 SAMPLES = 24

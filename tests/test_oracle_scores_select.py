@@ -3,9 +3,9 @@
 Row geometry: closed forms. Scores: integer-exact inputs (every fp32 sum exact),
 a hand-worked order example (tests/golden/score_sum_order.txt), an fp64 error
 bound, and a GQA-mapping probe. Selection: brute force over every tie pattern on
-tiny rows, plus the invariants that follow from the rule "every block strictly
-above the k-th score, ties to the highest index" (TensorRT-LLM PR #20276,
-Features, "Canonical QSA selection").
+tiny rows, plus the invariants of the canonical rule (TensorRT-LLM PR #20276,
+Features, "Canonical QSA selection" row): candidates scoring above the k-th
+largest value are kept, and equal scores rank by descending page index.
 """
 import itertools
 import math
