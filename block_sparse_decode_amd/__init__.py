@@ -20,7 +20,7 @@ __all__ = [
     "Plane", "qsa_rollback_stash_bytes", "qsa_rollback_gather", "qsa_rollback_restore", "qsa_step_slots",
     "QSA_DEVERR_SLOT",
     "QSA_DEVERR_PAGE_ID", "QSA_DEVERR_SEQ_LEN", "QSA_DEVERR_ROWS", "QSA_DEVERR_Q_RANGE",
-    "QSA_DEVERR_SELECTED", "DecodePlan", "qsa_plan_decode",
+    "QSA_DEVERR_SELECTED", "DecodePlan", "qsa_plan_decode", "qsa_select_sparse_decode_static",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +41,7 @@ EXPORTED = (
     "qsa_index_scores", "qsa_select_topk", "qsa_workspace_bytes", "qsa_sparse_decode", "qsa_select_sparse_decode",
     "qsa_kv_store", "qsa_rollback_stash_bytes", "qsa_step_slots", "qsa_rollback_gather", "qsa_rollback_restore",
     "qsa_nvfp4_dequant_pages", "qsa_status_string", "qsa_abi_version", "qsa_plan_decode",
+    "qsa_select_sparse_decode_static",
 )
 
 
@@ -139,6 +140,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_plan_decode.argtypes = [sp, I32, I32, ctypes.POINTER(DecodePlan)]
         L.qsa_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, I32, P, SZ, P]
         L.qsa_select_sparse_decode.argtypes = [sp, pp, P, P, P, P, P, P, I32, P, SZ, P]
+        L.qsa_select_sparse_decode_static.argtypes = [sp, pp, P, P, P, P, P, P, I32, P]
         L.qsa_kv_store.argtypes = [sp, pp, P, P, P]
         L.qsa_nvfp4_dequant_pages.argtypes = [sp, P, P, ctypes.c_float, P, I32, P, P]
         plp = ctypes.POINTER(Plane)
@@ -152,7 +154,7 @@ def lib() -> ctypes.CDLL:
         L.qsa_abi_version.restype = I32
         for name in ("qsa_index_scores", "qsa_select_topk", "qsa_sparse_decode", "qsa_select_sparse_decode",
                      "qsa_kv_store", "qsa_nvfp4_dequant_pages", "qsa_rollback_gather", "qsa_rollback_restore",
-                     "qsa_step_slots", "qsa_plan_decode"):
+                     "qsa_step_slots", "qsa_plan_decode", "qsa_select_sparse_decode_static"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -226,6 +228,13 @@ def qsa_select_sparse_decode(shape: Shape, paged: Paged, q, scores, selected, ou
                                           _ptr(selected), _ptr(out), _ptr(lse), _ptr(gate), int(num_splits),
                                           _ptr(workspace), int(workspace_bytes), _stream(stream)),
            "qsa_select_sparse_decode")
+
+
+def qsa_select_sparse_decode_static(shape: Shape, paged: Paged, q, scores, selected, out, lse=None,
+                                    num_splits: int = 0, stream=None, gate=None) -> None:
+    _check(lib().qsa_select_sparse_decode_static(ctypes.byref(shape), ctypes.byref(paged), _ptr(q), _ptr(scores),
+                                                 _ptr(selected), _ptr(out), _ptr(lse), _ptr(gate), int(num_splits),
+                                                 _stream(stream)), "qsa_select_sparse_decode_static")
 
 
 def qsa_kv_store(shape: Shape, paged: Paged, new_k, new_v, stream=None) -> None:

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["qsa_api.hip", "qsa_index.hip", "qsa_select.hip", "qsa_decode.hip", "qsa_store.hip", "qsa_rollback.hip"]
+SOURCES = ["qsa_api.hip", "qsa_index.hip", "qsa_select.hip", "qsa_decode.hip", "qsa_store.hip", "qsa_rollback.hip", "qsa_static.hip"]
 OUT = os.path.join(HERE, "libqsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -224,13 +224,15 @@ qsa_status qsa_plan_decode(const qsa_shape *sh, int32_t num_splits, int32_t fuse
 
 }  // extern "C"
 
-namespace {
+namespace qsa {
 
-// Shared by qsa_sparse_decode (scores == NULL: `selected` is an input) and
-// qsa_select_sparse_decode (the selection is computed from `scores` and written to `selected`).
+// Shared by qsa_sparse_decode (scores == NULL: `selected` is an input),
+// qsa_select_sparse_decode (the selection is computed from `scores` and written to `selected`)
+// and qsa_select_sparse_decode_static (clear_counters: the workspace's completion counters are
+// zeroed by a fill kernel before the attention launch, since its contents are not the caller's).
 qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const float *scores,
                        int32_t *selected, uint16_t *out, float *lse, const uint16_t *gate, int32_t num_splits,
-                       void *workspace, size_t workspace_bytes, void *stream)
+                       void *workspace, size_t workspace_bytes, void *stream, bool clear_counters)
 {
     qsa_status st = check_shape(sh);
     if (st != QSA_OK) return st;
@@ -301,7 +303,11 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     prm.v_global = pg->v_global;
     prm.gate = gate;
     prm.kv_format = sh->kv_format;
-    hipError_t e;
+    hipError_t e = hipSuccess;
+    if (clear_counters && need > 0) {
+        e = launch_clear_words(prm.counters, prm.tiles, (hipStream_t)stream);
+        if (e != hipSuccess) return QSA_ERR_HIP;
+    }
     if (!fused || KW == 0) {
         e = launch_sparse_decode(prm, sh->head_dim, (hipStream_t)stream);
     } else if (sh->max_pages <= 1024) {
@@ -327,7 +333,7 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
 }
 
-}  // namespace
+}  // namespace qsa
 
 extern "C" {
 
@@ -336,7 +342,7 @@ qsa_status qsa_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uin
                              size_t workspace_bytes, void *stream)
 {
     return decode_call(sh, pg, q, nullptr, const_cast<int32_t *>(selected), out, lse, gate, num_splits, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, false);
 }
 
 qsa_status qsa_select_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const float *scores,
@@ -345,7 +351,8 @@ qsa_status qsa_select_sparse_decode(const qsa_shape *sh, const qsa_paged *pg, co
 {
     if (sh && pg && sh->topk + sh->window > 0 && !scores && sh->num_rows > 0 && sh->num_requests > 0)
         return QSA_ERR_INVALID_ARG;
-    return decode_call(sh, pg, q, scores, selected, out, lse, gate, num_splits, workspace, workspace_bytes, stream);
+    return decode_call(sh, pg, q, scores, selected, out, lse, gate, num_splits, workspace, workspace_bytes, stream,
+                       false);
 }
 
 qsa_status qsa_kv_store(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *new_k, const uint16_t *new_v,

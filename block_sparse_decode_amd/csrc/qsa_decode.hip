@@ -817,6 +817,19 @@ hipError_t launch_select_sparse_decode(const DecodeParams &prm, int D, hipStream
     }
 }
 
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *p, int n)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_clear_words(uint32_t *p, int n, hipStream_t stream)
+{
+    if (n <= 0) return hipSuccess;
+    const int blocks = (n + 255) / 256 < 32 ? (n + 255) / 256 : 32;
+    clear_words_kernel<<<blocks, 256, 0, stream>>>(p, n);
+    return hipGetLastError();
+}
+
 // ---- parity hook: whole pages through the same decode as the attention kernel ----------
 template <int D>
 __global__ __launch_bounds__(256) void dequant_pages_kernel(DequantParams prm)

@@ -117,6 +117,14 @@ hipError_t launch_sparse_decode(const DecodeParams &prm, int D, hipStream_t stre
 // prologue (MP <= 1024); `selected` is written as qsa_select_topk writes it
 hipError_t launch_select_sparse_decode(const DecodeParams &prm, int D, hipStream_t stream);
 hipError_t launch_dequant_pages(const DequantParams &prm, int D, hipStream_t stream);
+// n uint32 words at p set to zero by a small fill kernel (no memset node in captured graphs)
+hipError_t launch_clear_words(uint32_t *p, int n, hipStream_t stream);
+
+// host side of the attention calls (qsa_api.hip): validation, launch plan and launches;
+// clear_counters zeroes the workspace's completion counters first
+qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t *q, const float *scores,
+                       int32_t *selected, uint16_t *out, float *lse, const uint16_t *gate, int32_t num_splits,
+                       void *workspace, size_t workspace_bytes, void *stream, bool clear_counters);
 hipError_t launch_kv_store(const StoreParams &prm, int D, int B, hipStream_t stream);
 
 // ---- rollback ---------------------------------------------------------------------------

@@ -235,6 +235,24 @@ qsa_status qsa_select_sparse_decode(const qsa_shape *shape, const qsa_paged *pag
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. qsa_select_sparse_decode without the
+ * workspace arguments: when the launch splits tiles, its counters and split partials live in
+ * an 8 MiB device array that the library holds on each GPU it runs on until the process
+ * ends (the call itself allocates nothing). Each call clears the counters it uses with a
+ * small fill kernel on `stream` before the attention launch. A shape whose split workspace
+ * (qsa_workspace_bytes(shape, num_splits)) exceeds 8 MiB returns QSA_ERR_WORKSPACE_TOO_SMALL
+ * before any launch; pass num_splits = 1 (no workspace) or use qsa_select_sparse_decode.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in time on one GPU
+ * (different streams, or graphs replayed concurrently) race and give wrong results. Other
+ * arguments, results and errors as for qsa_select_sparse_decode.
+ */
+qsa_status qsa_select_sparse_decode_static(const qsa_shape *shape, const qsa_paged *paged,
+                                           const uint16_t *q, const float *scores, int32_t *selected,
+                                           uint16_t *out, float *lse, const uint16_t *gate,
+                                           int32_t num_splits, void *stream);
+
+/*
  * The KV-store prologue of a step (PR #20276, Performance > What runs on the fast paths:
  * the decode prologue's index store and compression; PR #20937, What changes: a fused
  * decode prologue over NVFP4 KV). Writes this step's new tokens into the paged cache and
