@@ -169,6 +169,7 @@ qsa_status qsa_index_scores(const qsa_shape *sh, const qsa_paged *pg, const uint
     prm.Hkv = sh->num_kv_heads;
     prm.rmax = sh->max_rows_per_request;
     prm.sm_scale = sh->sm_scale;
+    prm.uniform_rows = (int64_t)sh->num_rows == (int64_t)sh->num_requests * sh->max_rows_per_request;
     hipError_t e = launch_index_scores(prm, sh->head_dim, sh->num_requests, (hipStream_t)stream);
     return e == hipSuccess ? QSA_OK : QSA_ERR_HIP;
 }
@@ -303,6 +304,11 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     prm.v_global = pg->v_global;
     prm.gate = gate;
     prm.kv_format = sh->kv_format;
+    prm.uniform_rows = (int64_t)sh->num_rows == (int64_t)sh->num_requests * sh->max_rows_per_request;
+    {
+        const int G = sh->num_q_heads / sh->num_kv_heads;
+        prm.one_row_tiles = G <= 16 ? prm.tile_cols == G : G % 16 == 0;
+    }
     hipError_t e = hipSuccess;
     if (clear_counters && need > 0) {
         e = launch_clear_words(prm.counters, prm.tiles, (hipStream_t)stream);

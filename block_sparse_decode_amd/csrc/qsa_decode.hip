@@ -42,6 +42,28 @@
 // and the output.
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
+
+// A traced build (-DQSA_TRACE) records, per wave of the first kTraceGroups workgroups of each
+// launch, the 100 MHz real-time clock at the points of the kernel named in trace_points
+// (a lane-0 vector store per point); qsa_trace_read copies them to the host. The normal
+// build has neither the stamps nor the buffer.
+#if defined(QSA_TRACE)
+namespace qsa {
+constexpr int kTraceGroups = 4096, kTracePoints = 16;
+__device__ unsigned long long qsa_trace_stamps[kTraceGroups * 8 * kTracePoints];
+__device__ __forceinline__ void trace_stamp(int k)
+{
+    const unsigned t = threadIdx.x;
+    if ((t & 63u) == 0u && blockIdx.x < (unsigned)kTraceGroups)
+        qsa_trace_stamps[((size_t)blockIdx.x * 8 + (t >> 6)) * kTracePoints + k] = __builtin_amdgcn_s_memrealtime();
+}
+}  // namespace qsa
+#define QSA_STAMP(k) qsa::trace_stamp(k)
+#else
+#define QSA_STAMP(k) ((void)0)
+#endif
+#define QSA_SELECT_STAMP(k) QSA_STAMP(k)
+
 #include "qsa_select_row.hpp"
 
 namespace qsa {
@@ -223,8 +245,15 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
 
 // SELC = 0: the rows' selections are an input. SELC = 2, 4, 8 or 16: they are computed here
 // from the scores (select_row with that many columns per lane) and also written out.
-template <int D, int SELC, int F>
-__global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(DecodeParams prm)
+// ONE: every tile holds columns of one row only (one-row tiles, or 16-column tiles of rows
+// of a multiple of 16 q heads), which the host knows from the launch shape. That form has a
+// shorter prologue of its own, and its instantiation carries none of the multi-row union
+// build, which leaves the compiler more registers for the rest.
+// Occupancy: one-row tiles come one workgroup per CU at most (the host groups rows whenever
+// the batch has more tiles than CUs), so their waves may take up to 256 registers; the
+// general form keeps 128, for two workgroups per CU on large grids.
+template <int D, int SELC, int F, bool ONE>
+__global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_kernel(DecodeParams prm)
 {
     constexpr int NW = kDecodeWaves;
     constexpr int NT = NW * 64;
@@ -252,6 +281,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     __shared__ uint32_t scan_tmp[NT / 64 + 1];
     __shared__ f16x8 q_lds[KS][64];         // the tile's q operand, in MFMA B-operand lane order
 
+    // The kernel arguments the prologue needs, all in scalar registers before anything waits
+    // on one: each first read of an argument's cache line misses the scalar cache at launch,
+    // and reading them where they are first used would chain several such misses (one per
+    // dependent step of the work-item arithmetic) before the first global load could issue.
+    asm volatile("" ::"s"(prm.tiles), "s"(prm.splits), "s"(prm.div_splits.m), "s"(prm.div_splits.l),
+                 "s"(prm.col_tiles), "s"(prm.Hkv), "s"(prm.div_htiles.m), "s"(prm.div_htiles.l),
+                 "s"(prm.div_ctiles.m), "s"(prm.div_ctiles.l), "s"(prm.row_offsets), "s"(prm.seq_lens),
+                 "s"(prm.uniform_rows), "s"(prm.rmax), "s"(prm.N), "s"(prm.tile_cols), "s"(prm.div_group.d),
+                 "s"(prm.div_group.m), "s"(prm.div_group.l), "s"(prm.MP), "s"(prm.KW), "s"(prm.page_table));
+    asm volatile("" ::"s"(SELC > 0 ? (const void *)prm.scores : (const void *)prm.selected), "s"(prm.q),
+                 "s"(prm.Hq), "s"(prm.log2P), "s"(prm.k), "s"(prm.W), "s"(prm.NP), "s"(prm.P));
     // work item i = tile * S + split, tiles numbered (request, KV head, column tile); XCD x
     // (the dispatcher's linear id mod 8) takes the contiguous items [x * per, (x + 1) * per)
     const int S = prm.splits;
@@ -261,18 +301,35 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     const uint32_t wg = blockIdx.x;
     const uint32_t item = (wg % kXcds) * per + wg / kXcds;
     if (item >= n_items) return;
+    QSA_STAMP(0);
     const int tile = (int)fast_div(item, prm.div_splits), s = (int)item - tile * S;
     const int T = prm.col_tiles;
     const int HT = prm.Hkv * T;
     const int b = (int)fast_div((uint32_t)tile, prm.div_htiles);
     const int g = (int)fast_div((uint32_t)(tile - b * HT), prm.div_ctiles), ct = tile - b * HT - g * T;
-    // the request's row range and length, both loads issued before either is waited on
-    const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
-    const int64_t Lb = prm.seq_lens[b];
+    // The request's row range and length. When every request has rmax rows (num_rows is
+    // B * rmax, which the host knows) the range is [b * rmax, (b + 1) * rmax) without a load,
+    // so the loads that depend on it issue at once; the row offsets are then only compared with
+    // it, off the critical path, by one thread per request. Otherwise both offsets are loaded
+    // before either is waited on.
     const int tid = threadIdx.x, lane = tid & 63;
+    const bool checker = tid == 0 && s == 0 && tile == b * HT;
+    int r0, r1, ro_check0 = 0, ro_check1 = 0;
+    if (prm.uniform_rows) {
+        r0 = b * prm.rmax;
+        r1 = r0 + prm.rmax;
+        if (checker) {
+            ro_check0 = prm.row_offsets[b];
+            ro_check1 = prm.row_offsets[b + 1];
+        }
+    } else {
+        r0 = prm.row_offsets[b];
+        r1 = prm.row_offsets[b + 1];
+    }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);     // wave-uniform, so in SGPRs
     const int gq = lane >> 4, li = lane & 15;
-    const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, tid == 0 && s == 0 && tile == b * HT);
+    const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, checker);
+    if (R >= 0) QSA_STAMP(1);           // (the condition makes the stamp wait for the row range)
     const int Rb = r1 - r0;         // the request's own row count fixes each row's length
     const int G = (int)prm.div_group.d;
     const int TW = prm.tile_cols;   // this tile: columns col0 .. col0 + TW - 1 of the request's R x G
@@ -303,10 +360,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     int32_t *pt_row = reinterpret_cast<int32_t *>(bm + nwords);
     uint32_t *owner = reinterpret_cast<uint32_t *>(pt_row + MP);
     const int nent = nrow * KW;                      // <= kMaxUnion
-    constexpr int kSelPerLane = kMaxUnion / 64;
+    constexpr int kSelPerLane = ONE ? 256 / 64 : kMaxUnion / 64;   // one row: k + W <= 256 entries
     int selp[kSelPerLane];
     int32_t *sel_lds = reinterpret_cast<int32_t *>(u_pm);   // the selections, before the union
-    const bool one_row = SELC > 0 && nrow == 1;
+    constexpr bool one_row = ONE && SELC > 0;        // fused selection, one row per tile
+    // one-row fused selection: per-lane masks and prefix counts (in wave 2's V staging tile)
+    // and the page-table entries of the row's columns (in wave 1's), until the union is placed
+    uint32_t *one_pub = reinterpret_cast<uint32_t *>(lds_area + 2 * (32 * D * 2));
+    int32_t *one_pt = reinterpret_cast<int32_t *>(lds_area + 1 * (32 * D * 2));
+    static_assert(SELC <= 16 && 64 * SELC * 4 <= 32 * D * 2, "one-row publish areas");
+    constexpr bool lean_one = ONE && SELC == 0;      // selection given, one row per tile
 
     // The independent global loads go first, so that no wave waits for one of them before
     // issuing the next: each selecting wave's score row (or wave 0's selection rows), the
@@ -353,24 +416,97 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qraw[ks] = qp[ks];
     }
-    if (!one_row) {
+    // the request's length: loaded only now, after the loads above have issued, so that
+    // waiting for it does not hold them back (nothing above needs it)
+    const int64_t Lb = prm.seq_lens[b];
+    if constexpr (!ONE) {
         for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
         for (int p = tid; p < MP; p += NT) {
             pt_row[p] = prm.page_table[(int64_t)b * MP + p];
             owner[p] = 0xffffffffu;
         }
     }
+    if constexpr (lean_one) {
+        if (wave == 0) {
+            // The row's listed pages, deduplicated and in ascending order (the order the fused
+            // selection lists them in), with a valid physical page. Each listed visible page's
+            // page-table entry is loaded at once (one dependent round trip for all of them);
+            // valid pages set their bit in a bitmap over the table and store their physical
+            // page beside it; the set bits, read back in ascending order with a prefix count
+            // for the positions, are the union. Wave 0 alone, so no workgroup barrier.
+            const RowGeom geo = row_geom(Lb, Rb, j_lo, prm.log2P, MP);
+            uint32_t *okmap = reinterpret_cast<uint32_t *>(lds_area);          // kMaxPages bits
+            int32_t *phys_of = reinterpret_cast<int32_t *>(okmap + kMaxPages / 32);
+            const int nbw = (MP + 31) >> 5;
+            int phv[kSelPerLane];
+#pragma unroll
+            for (int i = 0; i < kSelPerLane; ++i) {
+                const int p = selp[i];
+                const bool vis = lane + i * 64 < nent && p >= 0 && p < geo.pages;
+                phv[i] = vis ? prm.page_table[(int64_t)b * MP + p] : -1;
+            }
+            for (int w = lane; w < nbw; w += 64) okmap[w] = 0u;
+            wave_lds_fence();
+            const uint32_t npc = prm.NP < ((int64_t)1 << 31) ? (uint32_t)prm.NP : 0x80000000u;
+#pragma unroll
+            for (int i = 0; i < kSelPerLane; ++i) {
+                if (lane + i * 64 >= nent) continue;
+                const int p = selp[i];
+                if (p < -1 || p >= MP) {
+                    set_error(prm.err, QSA_DEVERR_SELECTED);
+                    continue;
+                }
+                const int ph = phv[i];
+                if (p < 0 || p >= geo.pages || ph == -1) continue;
+                if ((uint32_t)ph >= npc) {
+                    set_error(prm.err, QSA_DEVERR_PAGE_ID);
+                    continue;
+                }
+                phys_of[p] = ph;                          // duplicates store the same value
+                atomicOr(&okmap[p >> 5], 1u << (p & 31));
+            }
+            wave_lds_fence();
+            constexpr int kWordsPerLane = kMaxPages / 32 / 64;
+            uint32_t wm[kWordsPerLane];
+            uint32_t cnt = 0u;
+#pragma unroll
+            for (int t = 0; t < kWordsPerLane; ++t) {
+                const int wi = lane * kWordsPerLane + t;
+                wm[t] = wi < nbw ? okmap[wi] : 0u;
+                cnt += (uint32_t)__builtin_popcount(wm[t]);
+            }
+            const uint32_t incl = wave_inclusive_scan(cnt);
+            uint32_t pos = incl - cnt;
+            const int lenc = (int)min(geo.len, (int64_t)MP << prm.log2P);
+#pragma unroll
+            for (int t = 0; t < kWordsPerLane; ++t) {
+                uint32_t m = wm[t];
+                while (m) {
+                    const int p = (lane * kWordsPerLane + t) * 32 + __builtin_ctz(m);
+                    m &= m - 1u;
+                    const int vis = lenc - (p << prm.log2P);
+                    const int nc = vis >= P ? P / 32 : (vis + 31) / 32;
+                    u_pm[pos] = (uint32_t)p | (1u << 16) | ((uint32_t)nc << 24);
+                    u_phys[pos] = phys_of[p];
+                    ++pos;
+                }
+            }
+            if (lane == 63) scan_tmp[0] = incl;
+        }
+    }
     if constexpr (SELC > 0) {
-        if (one_row) {
+        if constexpr (one_row) {
             if (wave == 0) {
-                // The row's selection (into LDS, for the tile where the row starts, of KV
-                // head 0 and split 0, to publish after the barrier) and the union: the selected pages whose
-                // page-table entry is a valid physical page. Both lists are compacted without
-                // branches: one prefix scan gives both positions (selection count in the low
-                // half, union count in the high half), and a column that is in neither list
-                // writes a dump slot of its lane.
+                // The row's selection and its union (the selected pages whose page-table entry
+                // is a valid physical page) are placed by the whole workgroup after the
+                // barrier: a single wave placing every column itself would take hundreds of
+                // instructions while seven waves wait. This wave publishes, per lane, its
+                // columns' selection and union masks, their prefix counts over the lanes (one
+                // scan: selection count in the low half, union count in the high half) and the
+                // columns' page-table entries.
                 const RowGeom geo = row_geom(Lb, Rb, j_lo, prm.log2P, MP);
                 const uint32_t take = (uint32_t)select_row_take<SELC>(skey, geo.pages, prm.k, prm.W);
+                QSA_STAMP(4);
                 const uint32_t npc = prm.NP < ((int64_t)1 << 31) ? (uint32_t)prm.NP : 0x80000000u;
                 uint32_t ok = 0u, bad = 0u;
 #pragma unroll
@@ -384,28 +520,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
                 if (bad & take) set_error(prm.err, QSA_DEVERR_PAGE_ID);
                 const uint32_t cnt = (uint32_t)__builtin_popcount(take) | ((uint32_t)__builtin_popcount(ok) << 16);
                 const uint32_t incl = wave_inclusive_scan(cnt);
-                const uint32_t excl = incl - cnt;
-                const int c0 = lane * SELC;
-                const int lenc = (int)min(geo.len, (int64_t)MP << prm.log2P);
-                int32_t *sel_row = reinterpret_cast<int32_t *>(lds_area);   // KW entries, then dump slots
-                const int sel_dump = KW + lane, u_dump = kMaxUnion - 64 + lane;
+                one_pub[lane] = take | (ok << 16);
+                one_pub[64 + lane] = incl - cnt;
 #pragma unroll
-                for (int i = 0; i < SELC; ++i) {
-                    const uint32_t below = (1u << i) - 1u;
-                    const int p = c0 + i;
-                    const int spos = (int)((excl & 0xffffu) + (uint32_t)__builtin_popcount(take & below));
-                    const int upos = (int)((excl >> 16) + (uint32_t)__builtin_popcount(ok & below));
-                    const int vis = lenc - (p << prm.log2P);
-                    const int nc = vis >= P ? P / 32 : (vis + 31) / 32;
-                    sel_row[(take >> i) & 1u ? spos : sel_dump] = p;
-                    const int ui = (ok >> i) & 1u ? upos : u_dump;
-                    u_pm[ui] = (uint32_t)p | (1u << 16) | ((uint32_t)nc << 24);
-                    u_phys[ui] = ptv[i];
-                }
+                for (int i = 0; i < SELC; ++i) one_pt[lane * SELC + i] = ptv[i];
                 if (lane == 63) {
                     scan_tmp[0] = incl >> 16;
                     scan_tmp[1] = incl & 0xffffu;
                 }
+                QSA_STAMP(5);
             }
         } else if (wave < nrow) {
             // wave w selects the tile's row j_lo + w, into LDS
@@ -433,7 +556,30 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         }
         if (qbad) set_error(prm.err, QSA_DEVERR_Q_RANGE);
     }
+    QSA_STAMP(6);
     __syncthreads();
+    QSA_STAMP(7);
+    if constexpr (one_row) {
+        // every thread places up to two of the row's columns (64 * SELC <= 1024) in the
+        // selection row (ascending, in wave 0's V staging tile) and in the union
+        const int lenc = (int)min(row_geom(Lb, Rb, j_lo, prm.log2P, MP).len, (int64_t)MP << prm.log2P);
+        int32_t *sel_row = reinterpret_cast<int32_t *>(lds_area);
+        for (int c = tid; c < 64 * SELC; c += NT) {
+            const int ol = c / SELC, i = c % SELC;
+            const uint32_t pub = one_pub[ol], ex = one_pub[64 + ol];
+            const uint32_t tk = pub & 0xffffu, okm = pub >> 16, below = (1u << i) - 1u;
+            if ((tk >> i) & 1u) sel_row[(ex & 0xffffu) + (uint32_t)__builtin_popcount(tk & below)] = c;
+            if ((okm >> i) & 1u) {
+                const int upos = (int)((ex >> 16) + (uint32_t)__builtin_popcount(okm & below));
+                const int vis = lenc - (c << prm.log2P);
+                const int nc = vis >= P ? P / 32 : (vis + 31) / 32;
+                u_pm[upos] = (uint32_t)c | (1u << 16) | ((uint32_t)nc << 24);
+                u_phys[upos] = one_pt[c];
+            }
+        }
+        __syncthreads();
+        QSA_STAMP(12);
+    }
     if (one_row && wave == 0 && g == 0 && s == 0 && col0 <= j_lo * G) {
         // the row's selection, ascending, then -1 padding (before this wave's V staging
         // reuses the LDS copy)
@@ -443,7 +589,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         for (int i = lane; i < KW; i += 64) dst[i] = i < nsel ? sel_row[i] : -1;
         wave_lds_fence();
     }
-    if (!one_row) {
+    if constexpr (!ONE) {
     if (wave == 0) {
         if constexpr (SELC > 0) {
             // this workgroup publishes the rows that start in its tile (KV head 0, split 0)
@@ -540,6 +686,18 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     const uint32_t lco = (uint32_t)(li * code_bytes<D, F>() + gq * (code_bytes<D, F>() / 4));
     const uint32_t lso = (uint32_t)(li * scale_bytes<D, F>() + gq * (scale_bytes<D, F>() / 4));
 
+    // The q operand of S^T = K Q^T: held in registers by one-row tiles (which have them to
+    // spare), read from LDS per sub-chunk otherwise.
+    f16x8 qreg[ONE ? KS : 1];
+    if constexpr (ONE) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qreg[ks] = q_lds[ks][lane];
+    }
+    auto qop = [&](int ks) -> f16x8 {
+        if constexpr (ONE) return qreg[ks];
+        else return q_lds[ks][lane];
+    };
+
     // One register set: a sub-chunk's raw codes are consumed (K into the MFMA operands, V into
     // LDS) before the next sub-chunk's loads are issued into the same registers; those loads
     // are then in flight during the softmax and the P.V products.
@@ -556,7 +714,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
             sacc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_group<D, F>(kr[mt], ksc, ks), q_lds[ks][lane],
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dequant_group<D, F>(kr[mt], ksc, ks), qop(ks),
                                                                   sacc[mt], 0, 0, 0);
         }
 
@@ -631,11 +789,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
 
     UnitCursor u = seek_unit(u_lo + wave, u_hi, lc, u_pm, u_phys);
     if (u.have) load_unit<D, F>(prm, u.phys, g, u.c, lco, lso, kr, vr);
+    QSA_STAMP(8);
     while (u.have) {
         const UnitCursor un = seek_unit(u.u + NW, u_hi, lc, u_pm, u_phys);
         process(u, un, kr, vr);
         u = un;
     }
+    QSA_STAMP(9);
+    // (the offsets loaded at the start have long arrived; before any early return of a split)
+    if (prm.uniform_rows && checker && (ro_check0 != r0 || ro_check1 != r1)) set_error(prm.err, QSA_DEVERR_ROWS);
 
     // ---- 4. merge the waves (fixed order); wave w < d/16 finishes output tile w --------
     // Every wave publishes its column maxima and denominators, and in its own V staging tile
@@ -690,6 +852,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
         o_own = acc;
     }
     m_col = M;
+    QSA_STAMP(11);
     if (S > 1) {
         // Publish this split's partial (each owner its tile, wave 0 the denominators and the
         // column maxima), count it, and let the tile's last split merge. The partial moves
@@ -787,6 +950,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, 4) void sparse_decode_kernel(Dec
     }
     if (wave == 0 && gq == 0 && prm.lse)
         prm.lse[(int64_t)row * prm.Hq + head] = (Lsum > 0.0f) ? (m_col + __log2f(Lsum)) * 0.69314718055994531f : NEG_INF;
+    QSA_STAMP(10);
 }
 
 template <int D, int SELC>
@@ -794,10 +958,18 @@ static hipError_t launch_decode_d(const DecodeParams &prm, hipStream_t stream)
 {
     const int64_t per = ((int64_t)prm.tiles * prm.splits + kXcds - 1) / kXcds;   // work items per XCD
     const unsigned grid = (unsigned)(per * kXcds);
-    if (prm.kv_format == kFp8)
-        sparse_decode_kernel<D, SELC, kFp8><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
-    else
-        sparse_decode_kernel<D, SELC, kNvfp4><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+    const bool fp8 = prm.kv_format == kFp8;
+    if (prm.one_row_tiles) {
+        if (fp8)
+            sparse_decode_kernel<D, SELC, kFp8, true><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+        else
+            sparse_decode_kernel<D, SELC, kNvfp4, true><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+    } else {
+        if (fp8)
+            sparse_decode_kernel<D, SELC, kFp8, false><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+        else
+            sparse_decode_kernel<D, SELC, kNvfp4, false><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+    }
     return hipGetLastError();
 }
 
@@ -869,3 +1041,15 @@ hipError_t launch_dequant_pages(const DequantParams &prm, int D, hipStream_t str
 }
 
 }  // namespace qsa
+
+#if defined(QSA_TRACE)
+// Copies the first `count` stamps ([workgroup][wave][point], 100 MHz ticks) of the last traced
+// launch to host memory. Traced builds only.
+extern "C" int qsa_trace_read(unsigned long long *host, size_t count)
+{
+    const size_t cap = sizeof(qsa::qsa_trace_stamps) / sizeof(unsigned long long);
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(qsa::qsa_trace_stamps),
+                                    (count < cap ? count : cap) * sizeof(unsigned long long), 0,
+                                    hipMemcpyDeviceToHost);
+}
+#endif

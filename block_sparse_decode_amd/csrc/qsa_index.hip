@@ -68,14 +68,28 @@ __global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams pr
     // [element / 16][element mod 16][head], so that a chunk's eight heads are adjacent
     __shared__ __align__(16) float qs[NW][HG][16][NC];
 
+    // every kernel argument the prologue needs, in scalar registers before anything waits on
+    // one (each first read of an argument's cache line misses the scalar cache at launch)
+    asm volatile("" ::"s"(prm.row_offsets), "s"(prm.seq_lens), "s"(prm.page_table), "s"(prm.keys), "s"(prm.q32),
+                 "s"(prm.MP), "s"(prm.N), "s"(prm.rmax), "s"(prm.uniform_rows), "s"(prm.Hq), "s"(prm.Hkv),
+                 "s"(prm.W), "s"(prm.log2P), "s"(prm.NP));
     const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(wave);     // wave-uniform
-    // independent loads first: the row range, the request's length and this lane's page
-    const int r0 = prm.row_offsets[b], r1 = prm.row_offsets[b + 1];
-    const int64_t L_b = prm.seq_lens[b];
+    // independent loads first: the row range, the request's length and this lane's page. When
+    // every request has rmax rows (num_rows is B * rmax) the range is [b * rmax, (b + 1) * rmax)
+    // with no load, and the offsets are only compared with it at the end.
+    int r0, r1;
+    if (prm.uniform_rows) {
+        r0 = b * prm.rmax;
+        r1 = r0 + prm.rmax;
+    } else {
+        r0 = prm.row_offsets[b];
+        r1 = prm.row_offsets[b + 1];
+    }
     const int p = tile * kWave + lane;
     const int32_t phys = p < prm.MP ? prm.page_table[(int64_t)b * prm.MP + p] : -1;
+    const int64_t L_b = prm.seq_lens[b];
     // errors are reported at the end, after the loop
     const bool first = (j == 0 && tile == 0 && threadIdx.x == 0);
     const int R = clip_rows(r0, r1, prm.N, prm.rmax, prm.err, false);
@@ -245,6 +259,8 @@ __global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams pr
     if (first) {
         clip_rows(r0, r1, prm.N, prm.rmax, prm.err, true);
         if (L_b < r1 - r0 || L_b > (int64_t)prm.MP * prm.P) set_error(prm.err, QSA_DEVERR_SEQ_LEN);
+        if (prm.uniform_rows && (prm.row_offsets[b] != r0 || prm.row_offsets[b + 1] != r1))
+            set_error(prm.err, QSA_DEVERR_ROWS);
     }
 }
 

@@ -45,6 +45,7 @@ struct IndexParams {
     int64_t NP;
     int N, MP, P, log2P, W, Hq, Hkv, rmax;
     float sm_scale;
+    int uniform_rows;         // N == B * rmax: request b's rows are [b * rmax, (b + 1) * rmax)
 };
 
 struct SelectParams {
@@ -81,6 +82,8 @@ struct DecodeParams {
     float v_global;
     const uint16_t *gate;     // optional bf16 [N][Hq][d]: out = o * sigmoid(gate)
     int kv_format;            // QSA_KV_NVFP4 or QSA_KV_FP8
+    int uniform_rows;         // N == B * rmax: request b's rows are [b * rmax, (b + 1) * rmax)
+    int one_row_tiles;        // every tile holds columns of one row only
 };
 
 struct StoreParams {

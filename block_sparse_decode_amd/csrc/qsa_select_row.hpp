@@ -24,6 +24,11 @@
 
 #include "qsa_device.hpp"
 
+// Phase stamps of a traced build (see qsa_decode.hip); nothing otherwise.
+#ifndef QSA_SELECT_STAMP
+#define QSA_SELECT_STAMP(k) ((void)0)
+#endif
+
 namespace qsa {
 
 // Keys of the whole wave at or above t (wave-uniform): one ballot per register slot, all
@@ -96,10 +101,14 @@ __device__ __forceinline__ uint64_t select_row_take(uint32_t (&key)[C], int n, i
         key[i] = (p < wlo && !(s != s) && s != -__builtin_inff()) ? float_order_key(s) : 0u;
     }
     const uint32_t ncand = wave_count_ge<C>(key, 1u);
+    QSA_SELECT_STAMP(2);
 
     // 2. the k-th largest key T; keys above T are all taken, and krem of the keys equal
     //    to T (with krem = 0 no tie rule applies)
-    const uint32_t k = (uint32_t)k_;
+    // k in a register the compiler may not re-derive: under scalar-register pressure it would
+    // otherwise reload it from the kernel arguments (and wait for the load) in every bit step
+    uint32_t k = (uint32_t)k_;
+    asm volatile("" : "+s"(k));
     uint32_t T, krem = 0u;
     if (k == 0) {
         T = 0xffffffffu;                  // no key is above it: the window only
@@ -134,6 +143,8 @@ __device__ __forceinline__ uint64_t select_row_take(uint32_t (&key)[C], int n, i
             krem = k - ngt;               // >= 1
         }
     }
+
+    QSA_SELECT_STAMP(3);
 
     // 3. ties at T go to the highest pages: rank each tie by the ties at higher pages (later
     //    lanes, then later slots of this lane)

@@ -435,3 +435,23 @@ def test_graph_capture_replay():
         torch.cuda.synchronize()
         assert torch.equal(st.scores, eager[0]) and torch.equal(st.selected, eager[1])
         assert torch.equal(st.out, eager[2]) and torch.equal(st.lse, eager[3]), f"replay {i}"
+
+
+def test_uniform_rows_offsets_checked():
+    """When num_rows is B * max_rows, the kernels take request b's rows as [b * R, (b + 1) * R)
+    without waiting for row_offsets, and compare the offsets with that afterwards: offsets that
+    say otherwise set the ROWS bit, in the index scores and in both attention calls."""
+    cfg = synth.Config("uni_rows", 3, 4, 8, 2, 64, 64, (300, 2000), 4, 1, seed=309)
+    w = workload(cfg)
+    b = DeviceBatch.upload(w)
+    st = Step(b, num_splits=1)
+    st()
+    torch.cuda.synchronize()
+    assert int(b.error_word[0].item()) == 0
+    # the same total, split 3 + 5 + 4: still N == B * R, but request 0 has 3 rows
+    b.row_offsets.copy_(torch.tensor([0, 3, 8, 12], dtype=torch.int32))
+    for call in (st.scores_call, st.select_decode_call, st.decode_call):
+        b.error_word.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert int(b.error_word[0].item()) & q.QSA_DEVERR_ROWS, call.__name__
