@@ -194,53 +194,111 @@ def attention_flop(w, selected):
 
 
 def fused_kernel_name(w):
-    """Name rocprofv3 gives the fused selection + attention kernel for this workload."""
+    """Name rocprofv3 gives the fused selection + attention kernel for this workload, from the
+    launch plan the library reports (selection columns per lane, one-row tiles)."""
+    import block_sparse_decode_amd as q
+    from block_sparse_decode_amd.batch import DeviceBatch
     c = w.cfg
     fmt = 1 if getattr(c, "kv_format", "nvfp4") == "fp8" else 0
-    if w.MP > 1024:
-        return f"sparse_decode_kernel<{c.head_dim}, 0, {fmt}>"
-    return f"sparse_decode_kernel<{c.head_dim}, {8 if w.MP <= 512 else 16}, {fmt}>"
+    sh = q.Shape(int(w.B), int(w.N), max(1, int(w.max_rows)), c.q_heads, c.kv_heads, c.head_dim, c.page_size,
+                 int(w.MP), int(w.NP), c.topk, c.window, float(w.sm_scale), fmt)
+    plan = q.qsa_plan_decode(sh, 0, True)
+    G = c.q_heads // c.kv_heads
+    one = plan.tile_cols == G if G <= 16 else G % 16 == 0
+    return f"sparse_decode_kernel<{c.head_dim}, {plan.select_cols}, {fmt}, {'true' if one else 'false'}>"
 
 
-def cpu_baseline(w, max_rows):
-    """The CPU oracle (single-threaded C) on the first rows of the batch, scaled to a step."""
-    import numpy as np
-    import oracle
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _sub_workload(w, b0, b1):
+    """Requests [b0, b1) of a workload (whole requests, their rows and the shared pools)."""
     import synth
-    # a sub-batch of whole requests
+    r0, r1 = int(w.row_offsets[b0]), int(w.row_offsets[b1])
+    return synth.Workload(w.cfg, w.page_table[b0:b1], w.seq_lens[b0:b1], w.row_offsets[b0:b1 + 1] - r0,
+                          w.q[r0:r1], w.k_codes, w.k_scales, w.v_codes, w.v_scales, w.index_keys)
+
+
+def _oracle_step(sub):
+    import oracle
+    s = oracle.index_scores(sub)
+    sel = oracle.select_w(sub, s)
+    oracle.attention(sub, sel)
+
+
+def cpu_baseline(w, max_rows, runs=5):
+    """The CPU oracle (plain C, -O2, no fast-math) timed on this host: single-threaded on the
+    first requests (up to max_rows rows), median of `runs` runs; then the whole step with the
+    requests spread over every host thread (the oracle's calls release the interpreter lock,
+    and requests are independent), median of 3 runs. Both scaled to a step of w."""
+    import concurrent.futures
+    import statistics
     nb = 0
     while nb < w.B and int(w.row_offsets[nb + 1]) <= max_rows:
         nb += 1
     nb = max(1, nb)
     rows = int(w.row_offsets[nb])
-    sub = synth.Workload(w.cfg, w.page_table[:nb], w.seq_lens[:nb], w.row_offsets[:nb + 1],
-                         w.q[:rows], w.k_codes, w.k_scales, w.v_codes, w.v_scales, w.index_keys)
-    t0 = time.perf_counter()
-    s = oracle.index_scores(sub)
-    sel = oracle.select_w(sub, s)
-    oracle.attention(sub, sel)
-    dt = time.perf_counter() - t0
-    per_step_s = dt * w.N / rows
-    return per_step_s, rows, dt
+    sub = _sub_workload(w, 0, nb)
+    single = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        _oracle_step(sub)
+        single.append(time.perf_counter() - t0)
+    single_step = statistics.median(single) * w.N / rows
+    # this process's share of the host: the affinity mask, capped by OMP_NUM_THREADS where the
+    # environment sets it (a shared GPU host gives each GPU a share of its cores)
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = max(1, min(avail, cap if cap > 0 else avail, w.B))
+    parts = [_sub_workload(w, b, b + 1) for b in range(w.B)]
+    multi = []
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(ex.map(_oracle_step, parts))
+            multi.append(time.perf_counter() - t0)
+    return dict(single_step_s=single_step, single_rows=rows, single_runs=single, threads=threads,
+                multi_step_s=statistics.median(multi), multi_runs=multi, model=_cpu_model())
 
 
-def timed_us(fn, seq, stream, K):
-    """Mean µs per launch of fn over K back-to-back calls rotating through seq, between one HIP
+def timed_us(fn, seq, stream, K, reps=1):
+    """µs per launch of fn over K back-to-back calls rotating through seq, between one HIP
     event pair on the launch stream, after as many warmup calls (at least two per element of
     seq). A stage timed right after other, lighter stages otherwise starts below its steady
-    clock: the gated attention read 1.4 µs slow after a warmup of 32 calls (0.7 ms)."""
+    clock: the gated attention read 1.4 µs slow after a warmup of 32 calls (0.7 ms).
+    With reps > 1 the K calls are timed in `reps` batches and the batch means are returned."""
     import torch
     n = len(seq)
     for i in range(max(K, 2 * n)):
         fn(seq[i % n])
     torch.cuda.synchronize()
-    a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for i in range(K):
-        fn(seq[i % n])
-    b2.record(stream)
-    torch.cuda.synchronize()
-    return a.elapsed_time(b2) * 1e3 / K
+    per = max(1, K // reps)
+    out = []
+    for r in range(reps):
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(per):
+            fn(seq[(r * per + i) % n])
+        b2.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b2) * 1e3 / per)
+    return out if reps > 1 else out[0]
+
+
+def spread(xs):
+    """median, p10, p90 of a list of batch means (µs)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2)}
 
 
 def context_stage(args, q, synth, DeviceBatch, Step, dev, stream, K):
@@ -279,7 +337,8 @@ def main():
     ap.add_argument("--workload", default="mtp_verify_32k")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=48, help="rows of the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=8,
+                    help="rows of the single-threaded CPU-oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--context", action="store_true",
                     help="also time a context step (4 x 256 rows of 8K; its attention launches the same kernel as "
                          "the verify step, so it is off when profiling that kernel)")
@@ -341,14 +400,48 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # (2) each call alone, K back-to-back launches between one pair of HIP events on the
-    # launch stream (per-call events would add the event round trip to every launch)
-    def stage_us(fn):
-        return timed_us(fn, steps, stream, K)
-    fus_us = stage_us(lambda st: st.select_decode_call(stream))
-    dec_us = stage_us(lambda st: st.decode_call(stream))
-    idx_us = stage_us(lambda st: st.scores_call(stream))
-    sel_us = stage_us(lambda st: st.select_call(stream))
+    # (1b) the same steps replayed from one captured HIP graph (one step per layer copy)
+    graph = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        for st in steps:
+            st(gs)
+    stream.wait_stream(gs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        cur = torch.cuda.current_stream()
+        for st in steps:
+            st(cur)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps_g = max(2, K // len(steps))
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record()
+    for _ in range(reps_g):
+        graph.replay()
+    gb.record()
+    torch.cuda.synchronize()
+    graph_step_us = ga.elapsed_time(gb) * 1e3 / (reps_g * len(steps))
+    del graph
+
+    # (2) each call alone: back-to-back launches between one pair of HIP events on the launch
+    # stream (per-call events would add the event round trip to every launch), in 20 batches
+    # of 25 launches whose means give the median and the p10 / p90 spread; the mean over all
+    # batches is the stage's average launch time
+    STAGE_LAUNCHES, STAGE_REPS = 500, 20
+    spreads = {}
+
+    def stage_us(fn, name=None):
+        xs = timed_us(fn, steps, stream, STAGE_LAUNCHES, STAGE_REPS)
+        if name:
+            spreads[name] = spread(xs)
+        return sum(xs) / len(xs)
+    fus_us = stage_us(lambda st: st.select_decode_call(stream), "select_sparse_decode")
+    dec_us = stage_us(lambda st: st.decode_call(stream), "sparse_decode")
+    idx_us = stage_us(lambda st: st.scores_call(stream), "index_scores")
+    sel_us = stage_us(lambda st: st.select_call(stream), "select_topk")
 
     # (3) the KV store that precedes a step (this step's new K / V rows into the pools); run
     # last, since it rewrites the rows' slots and the touched pages' index keys
@@ -485,7 +578,11 @@ def main():
                    "fp8_select_sparse_decode_us": round(fp8_us, 2),
                    "fp8_select_attention_gbs": round(fp8_bytes / (fp8_us * 1e-6) / 1e9, 1),
                    **ctx_stages,
-                   "timing": "mean of back-to-back launches between one HIP event pair on the launch stream, after as many warmup launches"},
+                   "graph_step_us": round(graph_step_us, 2),
+                   "spread_us": spreads,
+                   "timing": "mean of back-to-back launches between HIP event pairs on the launch stream (20 batches "
+                             "of 25), after as many warmup launches; spread_us: median, p10, p90 of the batch means; "
+                             "graph_step_us: one step per layer copy replayed from a captured HIP graph"},
         "bytes": ab,
         "reference_copy_gbs": round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -494,11 +591,21 @@ def main():
         "error_word": err,
     }
     if args.cpu_rows > 0:
-        per_step_s, rows, dt = cpu_baseline(w, args.cpu_rows)
-        out["cpu_baseline"] = {"value": round(ab["step"] / per_step_s / 1e9, 4), "unit": "GB/s",
-                               "us_per_step": round(per_step_s * 1e6, 1), "cores": 1, "kind": "oracle",
-                               "sample": f"first {rows} of {w.N} rows (whole requests), all three stages, "
-                                         f"{dt:.1f} s single-threaded, scaled to the full step"}
+        cb = cpu_baseline(w, args.cpu_rows)
+        one = cb["single_step_s"]
+        allt = cb["multi_step_s"]
+        out["cpu_baseline"] = {
+            "value": round(ab["step"] / allt / 1e9, 4), "unit": "GB/s", "us_per_step": round(allt * 1e6, 1),
+            "cores": cb["threads"], "kind": "oracle", "cpu_model": cb["model"],
+            "sample": f"the whole step ({w.N} rows, all three stages) with the {w.B} requests spread over "
+                      f"{cb['threads']} host threads, median of 3 runs "
+                      f"({', '.join(f'{x:.2f}' for x in cb['multi_runs'])} s)",
+            "single_thread": {"value": round(ab["step"] / one / 1e9, 4), "unit": "GB/s",
+                              "us_per_step": round(one * 1e6, 1), "cores": 1,
+                              "sample": f"first {cb['single_rows']} of {w.N} rows (whole requests), median of "
+                                        f"{len(cb['single_runs'])} runs "
+                                        f"({', '.join(f'{x:.2f}' for x in cb['single_runs'])} s), scaled to the "
+                                        "full step"}}
     print(json.dumps(out), flush=True)
 
 

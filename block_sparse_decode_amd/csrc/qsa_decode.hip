@@ -280,6 +280,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     __shared__ float ml_l[NW][16];         // per wave: softmax denominators
     __shared__ uint32_t scan_tmp[NT / 64 + 1];
     __shared__ f16x8 q_lds[KS][64];         // the tile's q operand, in MFMA B-operand lane order
+    __shared__ int q_col_exp[16];           // per query column: its q operand is q * 2^-e
 
     // The kernel arguments the prologue needs, all in scalar registers before anything waits
     // on one: each first read of an argument's cache line misses the scalar cache at launch,
@@ -537,23 +538,42 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
         }
     }
     if (wave == NW - 1) {
+        // q into the f16 MFMA operand, each query column scaled by an exact power of two 2^-e
+        // that puts its largest |element| in [2^14, 2^15): no finite bf16 q overflows f16, and
+        // small columns keep all their bits. The column's logit scale takes the 2^e back
+        // (q_col_exp), so every logit is the same number as without the scaling. e is clamped
+        // so that the column's logit scale stays a normal fp32. A non-finite q element sets
+        // QSA_DEVERR_Q_RANGE (and propagates as in any arithmetic).
+        float f[KS][8];
+        float amax = 0.0f;
         bool qbad = false;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            f16x8 v = {};
-            if (colv) {
-                const uint4 raw = qraw[ks];
-                const float f[8] = {bf16lo(raw.x), bf16hi(raw.x), bf16lo(raw.y), bf16hi(raw.y),
-                                    bf16lo(raw.z), bf16hi(raw.z), bf16lo(raw.w), bf16hi(raw.w)};
+            const uint4 raw = qraw[ks];
+            f[ks][0] = bf16lo(raw.x); f[ks][1] = bf16hi(raw.x); f[ks][2] = bf16lo(raw.y); f[ks][3] = bf16hi(raw.y);
+            f[ks][4] = bf16lo(raw.z); f[ks][5] = bf16hi(raw.z); f[ks][6] = bf16lo(raw.w); f[ks][7] = bf16hi(raw.w);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) qbad |= !(fabsf(f[t]) <= 65504.0f);
-                const f16x2 h0 = {(half_t)f[0], (half_t)f[1]}, h1 = {(half_t)f[2], (half_t)f[3]};
-                const f16x2 h2 = {(half_t)f[4], (half_t)f[5]}, h3 = {(half_t)f[6], (half_t)f[7]};
-                v = __builtin_shufflevector(__builtin_shufflevector(h0, h1, 0, 1, 2, 3),
-                                            __builtin_shufflevector(h2, h3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+            for (int t = 0; t < 8; ++t) {
+                qbad |= !(fabsf(f[ks][t]) <= 3.4028234663852886e38f);
+                amax = fmaxf(amax, fabsf(f[ks][t]));
             }
+        }
+        amax = max_across_groups(amax);                 // the column's four lanes
+        int e = 0;
+        if (amax > 0.0f && amax <= 3.4028234663852886e38f) {
+            int ea, ec;
+            (void)frexpf(amax, &ea);                    // amax in [2^(ea-1), 2^ea)
+            (void)frexpf(prm.qk_scale_log2, &ec);
+            e = min(max(ea - 1 - 14, -125 - ec), 126 - ec);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            f16x8 v;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = (half_t)ldexpf(f[ks][t], -e);
             q_lds[ks][lane] = v;
         }
+        if (gq == 0) q_col_exp[li] = e;
         if (qbad) set_error(prm.err, QSA_DEVERR_Q_RANGE);
     }
     QSA_STAMP(6);
@@ -668,7 +688,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     const int lc = prm.log2P - 5;                   // log2(sub-chunks per page)
     const int NU = (int)U << lc;
     const int u_lo = S == 1 ? 0 : (int)(((int64_t)s * NU) / S), u_hi = S == 1 ? NU : (int)(((int64_t)(s + 1) * NU) / S);
-    const float c1 = prm.qk_scale_log2;
+    // this lane's column's logit scale: sm_scale * k_global * log2(e), times the 2^e its q
+    // operand was scaled down by (exact)
+    const float c1 = ldexpf(prm.qk_scale_log2, q_col_exp[li]);
     const float NEG_INF = -__builtin_inff();
 
     // O^T accumulators; tile NDT is a ones-row of V, so it accumulates sum_t P[t][col],

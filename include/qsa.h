@@ -56,7 +56,7 @@ typedef enum qsa_status {
 #define QSA_DEVERR_PAGE_ID    0x1u   /* a page-table entry outside [-1, NP): treated as -1 */
 #define QSA_DEVERR_SEQ_LEN    0x2u   /* seq_lens[b] < rows of b, or > MP * P: rows clipped */
 #define QSA_DEVERR_ROWS       0x4u   /* row_offsets not non-decreasing, or a request with > max rows */
-#define QSA_DEVERR_Q_RANGE    0x8u   /* a q element beyond the f16 range (|q| > 65504) */
+#define QSA_DEVERR_Q_RANGE    0x8u   /* a q element that is not finite (NaN or +-inf) */
 #define QSA_DEVERR_SELECTED   0x10u  /* a selected entry outside [-1, MP): ignored */
 #define QSA_DEVERR_SLOT       0x20u  /* a rollback row's slot outside [0, num_slots): skipped */
 
@@ -210,7 +210,9 @@ qsa_status qsa_plan_decode(const qsa_shape *shape, int32_t num_splits, int32_t f
  * The output is softmax(sm_scale * k_global * q . K_raw) @ (v_global * V_raw) over T, where
  * K_raw and V_raw are e2m1 * e4m3 (NVFP4) or e4m3 (FP8). An empty T gives out = 0 and lse = -inf. Each request's
  * rows share one read of the union of their selected pages. fp32 accumulation; the q and
- * P operands of the MFMA tiles are f16 (q must lie in the f16 range; see QSA_DEVERR_Q_RANGE).
+ * P operands of the MFMA tiles are f16: each query column's q is scaled by an exact power of
+ * two into the f16 range (its largest element in [2^14, 2^15)) and its logits are scaled
+ * back, so q of any finite bf16 magnitude is taken as is.
  * Deterministic for a fixed num_splits. sm_scale * k_global * log2(e) must be a positive
  * normal fp32 and v_global finite; otherwise QSA_ERR_INVALID_ARG.
  */

@@ -455,3 +455,44 @@ def test_uniform_rows_offsets_checked():
         call()
         torch.cuda.synchronize()
         assert int(b.error_word[0].item()) & q.QSA_DEVERR_ROWS, call.__name__
+
+
+@pytest.mark.parametrize("a", [100, 60, -20])
+def test_q_scaled_by_a_power_of_two(a):
+    """q * 2^a with sm_scale * 2^-a has the same logits: q far beyond f16's range (a = 100, 60)
+    and q in f16's subnormal range (a = -20) give the same scores, selections, outputs and lse,
+    bit for bit, as unscaled q, and the oracle's attention (each query column's q operand is
+    scaled into range by a power of two that its logit scale takes back)."""
+    cfg = synth.Config("q_pow2", 3, 4, 16, 2, 128, 64, (300, 3000), 5, 2, seed=310, invalid_frac=0.1)
+    w = workload(cfg)
+    ref_b = DeviceBatch.upload(w)
+    ref = Step(ref_b, num_splits=2)
+    ref()
+    w2 = dataclasses.replace(w)
+    w2.q = synth.bf16_bits_from_f32(synth.f32_from_bf16_bits(w.q) * np.float32(2.0 ** a))
+    assert np.array_equal(synth.f32_from_bf16_bits(w2.q), synth.f32_from_bf16_bits(w.q) * np.float32(2.0 ** a))
+    b2 = DeviceBatch.upload(w2)
+    b2.sm_scale = float(np.float32(w.sm_scale) * np.float32(2.0 ** -a))
+    for fused in (True, False):
+        st = Step(b2, num_splits=2, fused=fused)
+        st()
+        torch.cuda.synchronize()
+        assert torch.equal(st.scores, ref.scores) and torch.equal(st.selected, ref.selected), fused
+        assert torch.equal(st.out, ref.out) and torch.equal(st.lse, ref.lse), fused
+    assert int(b2.error_word[0].item()) == 0
+    sel = st.selected.cpu().numpy()
+    ref_out, ref_lse = oracle.attention(w2, sel, sm_scale=b2.sm_scale)
+    _check_attention(_u16(st.out), st.lse.cpu().numpy(), ref_out, ref_lse, f"q * 2^{a}")
+
+
+def test_non_finite_q_is_flagged():
+    """A q element that is not finite sets the Q_RANGE bit (the other rows are unaffected)."""
+    cfg = synth.Config("q_inf", 2, 2, 8, 2, 64, 64, (300, 2000), 4, 1, seed=311)
+    w = dataclasses.replace(workload(cfg))
+    w.q = w.q.copy()
+    w.q[1, 3, 5] = 0x7F80                          # +inf in bf16
+    b, st = _run(w, num_splits=1)
+    assert int(b.error_word[0].item()) & q.QSA_DEVERR_Q_RANGE
+    good = [r for r in range(w.N) if r != 1]
+    ref_out, ref_lse = oracle.attention(w, st.selected.cpu().numpy())
+    _check_attention(_u16(st.out)[good], st.lse.cpu().numpy()[good], ref_out[good], ref_lse[good], "q inf")
