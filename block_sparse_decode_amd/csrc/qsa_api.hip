@@ -1,6 +1,7 @@
 // qsa_api.hip -- the C ABI of libqsa (declared in include/qsa.h): host-side validation,
 // launch-shape choice and kernel launches. No allocation, no synchronisation, no global state.
 #include <cfloat>
+#include <cmath>
 #include <math.h>
 #include <algorithm>
 #include <stddef.h>
@@ -50,25 +51,51 @@ qsa_status check_rows_ptrs(const qsa_paged *pg)
 }
 
 constexpr int kCUs = 256;
+// A tile's prologue (row range, selection, union) in units of one page's loop work: the
+// 32K verify workload's fused prologue (about 4.6 us) against its loop (about 11 us for a
+// row's 34 pages).
+constexpr double kTileProloguePages = 14.0;
 
 // Query columns per tile. A request's columns for one KV head are its R rows x G q heads
 // (row-major); a tile is a run of at most 16 of them (one MFMA N tile), and every page
-// that any of the tile's rows selected is read once for the whole tile. Tiles hold whole
-// rows when G <= 16. Grouping more rows per tile saves reads of pages that several rows
-// selected, but leaves fewer independent tiles; when the batch has fewer tiles than CUs
-// the remaining parallelism must come from splitting a tile's pages across workgroups,
-// which costs a merge of the splits. So rows per tile are halved while that keeps too
-// few tiles, down to one row.
+// that any of the tile's rows selected is dequantised once for the whole tile. Tiles hold
+// whole rows when G <= 16.
+//
+// Rows per tile, r, trade that sharing against balance. A tile's cost is taken as its
+// expected union of pages plus a fixed prologue, and a launch of T tiles as ceil(T / CUs)
+// times that: tiles are counted in rounds of one per CU, since a CU that holds two tiles
+// finishes when both have. The union of r rows, each selecting s = k + W of a request's n
+// pages (n taken as the table width MP), is n (1 - (1 - s/n)^r) when the selections are
+// independent: verify rows of a long request share only their window and a few pages,
+// the neighbouring rows of a context step over a short one most of theirs. A larger r is
+// considered only while it keeps a tile per CU; below that the parallelism has to come
+// from splits (auto_splits), whose merge a single row per tile avoids best. Measured
+// (MI355X, fused launch): 48 requests x 4 verify rows over 1024-page tables, one row per
+// tile 53.8 us against 56.0 us at two; 4 requests x 256 context rows over 128 pages, two
+// rows per tile 140 us against 158 us at one.
 int tile_cols(const qsa_shape *sh)
 {
     const int G = sh->num_q_heads / sh->num_kv_heads;
     if (G >= 16) return 16;
-    int rows = std::max(1, std::min({sh->max_rows_per_request, 16 / G, kTileMaxRows}));
+    const int rcap = std::max(1, std::min({sh->max_rows_per_request, 16 / G, kTileMaxRows}));
     auto tiles = [&](int r) {
         return (int64_t)sh->num_requests * sh->num_kv_heads * ((sh->max_rows_per_request + r - 1) / r);
     };
-    while (rows > 1 && tiles(rows) < kCUs) rows = (rows + 1) / 2;
-    return rows * G;
+    const double n = std::max(1, sh->max_pages);
+    const double sel = std::min<double>(sh->topk + sh->window, n);
+    int best = 1;
+    double best_cost = 0.0;
+    for (int r = 1; r <= rcap; ++r) {
+        const int64_t T = tiles(r);
+        if (r > 1 && T < kCUs) break;
+        const double uni = n * (1.0 - std::pow(1.0 - sel / n, (double)r));
+        const double cost = (double)((T + kCUs - 1) / kCUs) * (uni + kTileProloguePages);
+        if (r == 1 || cost < best_cost) {
+            best = r;
+            best_cost = cost;
+        }
+    }
+    return best * G;
 }
 
 int col_tiles(const qsa_shape *sh)

@@ -330,6 +330,11 @@ int main(void) {
     (64, 3, 20, 4, 64, 3, 15, 1),      # 3 rows x 5 q heads
     (8, 4, 16, 4, 64, 1, 4, 4),        # few tiles: rows halved down to one
     (8, 2, 48, 2, 64, 0, 16, 3),       # 24 q heads per KV head: tiles cut rows
+    # verify rows over 1024-page tables share few pages: 768 one-row tiles (3 rounds of the
+    # CUs) beat 384 two-row ones (2 rounds of tiles with twice the union)
+    (48, 4, 32, 4, 1024, 1, 8, 4),
+    # a context step's neighbouring rows over 128 pages share most of theirs: two rows per tile
+    (4, 256, 32, 4, 128, 2, 16, 128),
 ])
 def test_plan_tile_heights(B, R, Hq, Hkv, MP, rows, cols, ctiles):
     sh = _shape(num_requests=B, num_rows=B * R, max_rows_per_request=R, num_q_heads=Hq, num_kv_heads=Hkv,
@@ -338,7 +343,7 @@ def test_plan_tile_heights(B, R, Hq, Hkv, MP, rows, cols, ctiles):
     assert (p.rows_per_tile, p.tile_cols, p.col_tiles) == (rows, cols, ctiles)
     assert p.workspace_bytes == q.qsa_workspace_bytes(sh, 0)
     assert p.workgroups % 8 == 0 and p.workgroups >= B * Hkv * ctiles * p.splits
-    assert p.select_cols == (2 if MP <= 128 else 8)
+    assert p.select_cols == (2 if MP <= 128 else 4 if MP <= 256 else 8 if MP <= 512 else 16)
     assert q.qsa_plan_decode(sh, 0, False).select_cols == 0
     assert q.qsa_plan_decode(sh, 3, True).splits == 3
 
