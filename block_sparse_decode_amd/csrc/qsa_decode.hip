@@ -249,9 +249,9 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
 // of a multiple of 16 q heads), which the host knows from the launch shape. That form has a
 // shorter prologue of its own, and its instantiation carries none of the multi-row union
 // build, which leaves the compiler more registers for the rest.
-// Occupancy: one-row tiles come one workgroup per CU at most (the host groups rows whenever
-// the batch has more tiles than CUs), so their waves may take up to 256 registers; the
-// general form keeps 128, for two workgroups per CU on large grids.
+// Occupancy: LDS allows two workgroups per CU. The one-row form is allowed up to 256
+// registers per lane but takes about 126, so two of its workgroups still fit a CU; the
+// general form is held to 128.
 template <int D, int SELC, int F, bool ONE>
 __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_kernel(DecodeParams prm)
 {
