@@ -356,7 +356,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the path shards by request with no exchange, see DESIGN.md", file=sys.stderr)
+              "requests are independent, so a deployment shards them across GPUs with no exchange", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
