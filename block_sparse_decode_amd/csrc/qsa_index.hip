@@ -73,7 +73,20 @@ __global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams pr
     asm volatile("" ::"s"(prm.row_offsets), "s"(prm.seq_lens), "s"(prm.page_table), "s"(prm.keys), "s"(prm.q32),
                  "s"(prm.MP), "s"(prm.N), "s"(prm.rmax), "s"(prm.uniform_rows), "s"(prm.Hq), "s"(prm.Hkv),
                  "s"(prm.W), "s"(prm.log2P), "s"(prm.NP));
-    const int tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    // Page tile of this workgroup. The dispatcher deals workgroups to the 8 XCDs by linear id,
+    // so with the tile index fastest, tile x of every row lands on XCD x mod 8 whenever the
+    // tiles per row are a multiple of 8. Tiles past a short request's pages leave at once, so
+    // the low tiles carry most of the work, and on a batch of mixed lengths the low XCDs
+    // would get most of it. Request b therefore rotates its tiles by b within each aligned
+    // group of 8 (a partial last group is left as it is): a bijection of the row's tiles that
+    // spreads the live ones over the XCDs and keeps the rows of one (request, tile) on one
+    // XCD, where they share the tile's keys.
+    const int j = blockIdx.y, b = blockIdx.z;
+    const int x = blockIdx.x;
+    // (the tile count from MP, an argument already in registers: gridDim would be read from
+    // the dispatch packet, one more scalar-cache miss ahead of the page-table load)
+    const int tiles_per_row = (prm.MP + kWave - 1) / kWave;
+    const int tile = ((x | 7) < tiles_per_row) ? ((x & ~7) | ((x + b) & 7)) : x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(wave);     // wave-uniform
     // independent loads first: the row range, the request's length and this lane's page. When
