@@ -13,10 +13,10 @@
 // splitting a tile's pages instead costs a merge.
 //  1. The tile's rows (at most 4 causal rows: verify rows, or a run of a context step's
 //     rows) each list their selected pages (computed here from the scores, one wave per
-//     row, when the selection is fused in). Wave 0 builds the union of those pages, each
-//     with a row bitmask, in LDS, and drops entries whose page-table entry is -1. Each page
-//     of the union is read once for all the tile's rows. A one-row tile with the selection
-//     fused in has its selecting wave write the union directly.
+//     row, when the selection is fused in). The workgroup builds the union of those pages in
+//     ascending order, each with a row bitmask, in LDS, and drops entries whose page-table
+//     entry is -1. Each page of the union is read once for all the tile's rows. A one-row
+//     tile with the selection fused in has its selecting wave publish the union directly.
 //  2. The union's 32-token sub-chunks are numbered page-major. Split s takes a contiguous
 //     range of them and its waves deal that range round-robin, so waves differ by at most
 //     one sub-chunk. Each wave runs an online softmax over its sub-chunks:
@@ -70,6 +70,7 @@ namespace qsa {
 
 constexpr int kMaxUnion = 1024;     // rows (<= 4) x (k + W) (<= 256)
 constexpr int kMaxPages = 4096;     // page-table stride MP
+constexpr int kTileRows = 4;        // rows of a multi-row tile
 constexpr int kXcds = kXcdCount;
 
 __device__ __forceinline__ void wave_lds_fence()
@@ -268,10 +269,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     static_assert(SELC <= 32, "a one-row tile's selection mask is kept in 32 bits");
     static_assert(D / 8 <= 16, "one V row holds at most 16 swizzled chunks");
 
-    // One LDS area: the union build's scratch (row-mask bitmap, page-table row, owner of each
-    // page), then the per-wave V staging tiles, then the wave merge slots.
+    // One LDS area: the union build's scratch (row-mask bitmap, page-table row), then the
+    // per-wave V staging tiles, then the wave merge slots.
     constexpr int kStageBytes = NW * 32 * D * 2;
-    constexpr int kScratchBytes = 4 * (kMaxPages / 4 + 2 * kMaxPages);
+    constexpr int kScratchBytes = 4 * (kMaxPages / 4 + kMaxPages);
     __shared__ __attribute__((aligned(16))) char lds_area[kStageBytes > kScratchBytes ? kStageBytes : kScratchBytes];
     half_t(*vsm)[32 * D] = reinterpret_cast<half_t(*)[32 * D]>(lds_area);
     __shared__ uint32_t u_pm[kMaxUnion];    // page | row mask << 16 | sub-chunks << 24
@@ -343,14 +344,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
 
     // ---- 1. union of the tile's rows' selected pages; the q operand ------------------
     // All threads stage this request's page-table row in LDS (scratch in the V staging
-    // area, with a row-mask bitmap of one byte per page and an owner word per page) while
-    // the selecting waves load their score rows (or wave 0 the selection rows) and the last
-    // wave loads q, so the union costs one dependent global round trip. Then wave 0 alone
-    // builds the union: each listed page ORs its row into the bitmap and bids its entry
-    // index for the page's owner word (the smallest bid wins), and each page's owner
-    // appends it, with ballot counts for the positions, so no workgroup barrier is needed.
-    // The last wave converts q into the MFMA B operand in LDS before the first barrier. Union
-    // order: by first listing (rows in order), a function of the input alone.
+    // area, with a row-mask bitmap of one byte per page) while the selecting waves load their
+    // score rows (or every thread its share of the selection rows) and the last wave loads q,
+    // so the union costs one dependent global round trip. After the first barrier every
+    // thread marks its entries' pages in the bitmap, and after a second one wave 0 lists the
+    // marked pages. The last wave converts q into the MFMA B operand in LDS before the first
+    // barrier. Union order: ascending page, as for one-row tiles.
     // A one-row tile with the selection fused in takes a shorter way: its selecting wave
     // holds the page-table entries of its columns in registers beside the score keys and
     // writes the union itself (the selected pages with a valid physical page, ascending, as
@@ -359,9 +358,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     const int nwords = ((MP + 3) / 4 + 3) & ~3;
     uint32_t *bm = reinterpret_cast<uint32_t *>(lds_area);
     int32_t *pt_row = reinterpret_cast<int32_t *>(bm + nwords);
-    uint32_t *owner = reinterpret_cast<uint32_t *>(pt_row + MP);
     const int nent = nrow * KW;                      // <= kMaxUnion
-    constexpr int kSelPerLane = ONE ? 256 / 64 : kMaxUnion / 64;   // one row: k + W <= 256 entries
+    // the selection entries a thread holds: one row's k + W <= 256 entries over wave 0's lanes
+    // (one-row tiles), or the tile's nrow * (k + W) <= 1024 entries over all 512 threads
+    constexpr int kSelPerLane = ONE ? 256 / 64 : kMaxUnion / NT;
     int selp[kSelPerLane];
     int32_t *sel_lds = reinterpret_cast<int32_t *>(u_pm);   // the selections, before the union
     constexpr bool one_row = ONE && SELC > 0;        // fused selection, one row per tile
@@ -379,9 +379,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     if constexpr (SELC == 0) {
 #pragma unroll
         for (int i = 0; i < kSelPerLane; ++i) {
-            const int idx = lane + i * 64;
+            const int idx = ONE ? lane + i * 64 : tid + i * NT;
             selp[i] = -1;
-            if (wave == 0 && idx < nent) {
+            if ((ONE ? wave == 0 : true) && idx < nent) {
                 const int jr = (int)fast_div((uint32_t)idx, prm.div_kw);
                 selp[i] = prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)];
             }
@@ -422,10 +422,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     const int64_t Lb = prm.seq_lens[b];
     if constexpr (!ONE) {
         for (int w = tid; w < nwords; w += NT) bm[w] = 0u;
-        for (int p = tid; p < MP; p += NT) {
-            pt_row[p] = prm.page_table[(int64_t)b * MP + p];
-            owner[p] = 0xffffffffu;
-        }
+        for (int p = tid; p < MP; p += NT) pt_row[p] = prm.page_table[(int64_t)b * MP + p];
     }
     if constexpr (lean_one) {
         if (wave == 0) {
@@ -610,71 +607,83 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
         wave_lds_fence();
     }
     if constexpr (!ONE) {
-    if (wave == 0) {
-        if constexpr (SELC > 0) {
-            // this workgroup publishes the rows that start in its tile (KV head 0, split 0)
+        // The union of the tile's rows, in two steps. Every thread marks up to two of the tile's
+        // nrow * (k + W) selection entries: a listed page that its row can see and whose
+        // page-table entry is a valid physical page sets the row's bit in the page's byte of the
+        // bitmap (a page listed twice sets it twice). Then wave 0 lists the marked pages in
+        // ascending order, each with its row mask and the sub-chunks its longest requesting row
+        // can see, with a wave prefix count per 64 words of the bitmap for the positions.
+        // The rows' page counts and lengths are the same for every entry, so they are taken once.
+        int rpages[kTileRows], rlen[kTileRows];
+        const int64_t lfull_p = (int64_t)MP << prm.log2P;
 #pragma unroll
-            for (int i = 0; i < kSelPerLane; ++i) {
-                const int idx = lane + i * 64;
-                selp[i] = -1;
-                if (i * 64 >= nent) break;
-                if (idx < nent) {
-                    selp[i] = sel_lds[idx];
-                    const int jr = (int)fast_div((uint32_t)idx, prm.div_kw);
-                    if (g == 0 && s == 0 && col0 <= (j_lo + jr) * G)
-                        prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)] = selp[i];
-                }
-            }
-            wave_lds_fence();        // the reads of sel_lds are done before u_pm is written
+        for (int r = 0; r < kTileRows; ++r) {
+            const RowGeom geo = row_geom(Lb, Rb, j_lo + min(r, nrow - 1), prm.log2P, MP);
+            rpages[r] = geo.pages;
+            rlen[r] = (int)min(geo.len, lfull_p);
         }
-        int phys_e[kSelPerLane];
+        auto of_row = [&](const int (&v)[kTileRows], int r) {
+            return r == 0 ? v[0] : r == 1 ? v[1] : r == 2 ? v[2] : v[3];
+        };
+        const uint32_t npc = prm.NP < ((int64_t)1 << 31) ? (uint32_t)prm.NP : 0x80000000u;
 #pragma unroll
         for (int i = 0; i < kSelPerLane; ++i) {
-            phys_e[i] = -1;
-            const int idx = lane + i * 64;
-            if (i * 64 >= nent) break;
-            if (idx >= nent) continue;
+            const int idx = tid + i * NT;
+            if (idx >= nent) break;
             const int jr = (int)fast_div((uint32_t)idx, prm.div_kw);
-            const int p = selp[i];
+            int p;
+            if constexpr (SELC > 0) {
+                p = sel_lds[idx];
+                // this workgroup publishes the rows that start in its tile (KV head 0, split 0)
+                if (g == 0 && s == 0 && col0 <= (j_lo + jr) * G)
+                    prm.selected[(int64_t)(r0 + j_lo + jr) * KW + (idx - jr * KW)] = p;
+            } else {
+                p = selp[i];
+            }
             if (p < -1 || p >= MP) {
                 set_error(prm.err, QSA_DEVERR_SELECTED);
                 continue;
             }
-            if (p < 0 || p >= row_geom(Lb, Rb, j_lo + jr, prm.log2P, MP).pages) continue;   // no visible token
+            if (p < 0 || p >= of_row(rpages, jr)) continue;      // no visible token
             const int phys = pt_row[p];
             if (phys == -1) continue;
-            if (phys < -1 || (int64_t)phys >= prm.NP) {
+            if ((uint32_t)phys >= npc) {                          // below -1 or past the pool
                 set_error(prm.err, QSA_DEVERR_PAGE_ID);
                 continue;
             }
-            phys_e[i] = phys;
             atomicOr(&bm[p >> 2], 1u << ((p & 3) * 8 + jr));
-            atomicMin(&owner[p], (uint32_t)idx);
         }
-        wave_lds_fence();
-        uint32_t nu = 0;
+        __syncthreads();             // every mark is in; the selections' LDS copy is read
+        if (wave == 0) {
+            const int nw = (MP + 3) / 4;                          // bitmap words, 4 pages each
+            uint32_t base = 0u;
+            for (int t = 0; t * 64 < nw; ++t) {
+                const int wi = t * 64 + lane;
+                const uint32_t x = wi < nw ? bm[wi] : 0u;
+                uint32_t y = x | (x >> 4);
+                y |= y >> 2;
+                y |= y >> 1;
+                y &= 0x01010101u;                                 // bit 8k: page 4 wi + k is marked
+                const uint32_t cnt = (uint32_t)__builtin_popcount(y);
+                const uint32_t incl = wave_inclusive_scan(cnt);
+                uint32_t pos = base + incl - cnt;
 #pragma unroll
-        for (int i = 0; i < kSelPerLane; ++i) {
-            if (i * 64 >= nent) break;
-            const int idx = lane + i * 64;
-            const int p = selp[i];
-            const bool own = phys_e[i] >= 0 && owner[p] == (uint32_t)idx;
-            const uint64_t bal = __ballot(own);
-            if (own) {
-                const uint32_t pos = nu + (uint32_t)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
-                const uint32_t m = (bm[p >> 2] >> ((p & 3) * 8)) & 0xffu;
-                // sub-chunks of 32 tokens that the longest requesting row can see
-                const int jmax = j_lo + 31 - __builtin_clz(m);     // later rows see more tokens
-                const int64_t vis = row_geom(Lb, Rb, jmax, prm.log2P, MP).len - ((int64_t)p << prm.log2P);
-                const int nc = (int)(vis >= P ? P / 32 : (vis + 31) / 32);
-                u_pm[pos] = (uint32_t)p | (m << 16) | ((uint32_t)nc << 24);
-                u_phys[pos] = phys_e[i];
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t m = (x >> (8 * k)) & 0xffu;
+                    if (m == 0u) continue;
+                    const int p = wi * 4 + k;
+                    const int jmax = 31 - __builtin_clz(m);            // later rows see more tokens
+                    const int vis = of_row(rlen, jmax) - (p << prm.log2P);
+                    const int nc = vis >= P ? P / 32 : (vis + 31) / 32;
+                    u_pm[pos] = (uint32_t)p | (m << 16) | ((uint32_t)nc << 24);
+                    u_phys[pos] = pt_row[p];
+                    ++pos;
+                }
+                base += __builtin_amdgcn_readlane(incl, 63);
             }
-            nu += (uint32_t)__builtin_popcountll(bal);
+            if (lane == 0) scan_tmp[0] = base;
         }
-        if (lane == 0) scan_tmp[0] = nu;
-    }
-    __syncthreads();                 // union list ready; the scratch area becomes V staging
+        __syncthreads();             // union list ready; the scratch area becomes V staging
     }
     const uint32_t U = scan_tmp[0];
     // The lane's bit in a page's row mask (bit 8, always set below, for a padding column) and
