@@ -3,7 +3,8 @@ workspace is the library's own device array) against qsa_select_sparse_decode wi
 workspace, through the C ABI: the same selection rows and the same outputs, bit for bit (the
 same kernels at the same split count), and the oracle's attention within tolerance. Two calls
 in a row, the second on a smaller batch with a different split count, so the second call runs
-on what the first left in the array.
+on what the first left in the array. A graph test captures the static call with the index scores
+and replays it between eager calls of the program's own.
 """
 import numpy as np
 import pytest
@@ -95,3 +96,56 @@ def test_static_entry_point_gated_split():
                                       gate=gate)
     torch.cuda.synchronize()
     assert torch.equal(out, ref.out)
+
+
+def test_static_entry_point_in_a_graph():
+    """The callers it is for include code under HIP graph capture: the index scores and the
+    static call captured in one graph, replayed four times with eager work of the program's own
+    (refilled outputs, another call of the static entry point on a different batch, which
+    leaves its own contents in the array) and synchronisations between the replays. Every
+    replay equals the eager step bit for bit; the counters are cleared inside the graph by a
+    fill kernel, not a memset node."""
+    w = synth.generate(synth.Config("na_graph", 5, 4, 16, 2, 128, 64, (300, 4000), 6, 2, seed=955,
+                                    invalid_frac=0.1))
+    other = synth.generate(synth.Config("na_other", 2, 2, 8, 2, 64, 64, (200, 2000), 4, 1, seed=956))
+    b, bo = DeviceBatch.upload(w), DeviceBatch.upload(other)
+    splits = 3
+    st = Step(b, num_splits=splits)
+    so = Step(bo, num_splits=2)
+    sel = torch.full_like(st.selected, -7)
+    out = torch.full_like(st.out, 0x1234)
+    lse = torch.full_like(st.lse, 3.0)
+
+    def step(stream):
+        st.scores_call(stream)
+        q.qsa_select_sparse_decode_static(st.shape_, st.paged_, b.q, st.scores, sel, out, lse, splits, stream)
+
+    step(None)
+    torch.cuda.synchronize()
+    eager = (st.scores.clone(), sel.clone(), out.clone(), lse.clone())
+    ref = Step(b, num_splits=splits)
+    ref()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref.out) and torch.equal(lse, ref.lse) and torch.equal(sel, ref.selected)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(torch.cuda.current_stream())
+    for i in range(4):
+        out.fill_(0x1234)
+        sel.fill_(-7)
+        lse.fill_(3.0)
+        st.scores.fill_(1.0)
+        so.scores_call()
+        q.qsa_select_sparse_decode_static(so.shape_, so.paged_, bo.q, so.scores, so.selected, so.out, so.lse, 2)
+        torch.cuda.synchronize()
+        print(f"[no-alloc] graph replay {i}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.scores, eager[0]) and torch.equal(sel, eager[1]), f"replay {i}"
+        assert torch.equal(out, eager[2]) and torch.equal(lse, eager[3]), f"replay {i}"
