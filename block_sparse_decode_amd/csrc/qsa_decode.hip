@@ -397,10 +397,24 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
             // columns, all inside the row, are read
             const int c0 = lane * SELC;
             const int32_t *ptr = prm.page_table + (int64_t)b * MP;
+            if (SELC >= 4 && (MP & 3) == 0 && c0 + SELC <= MP) {
+                // 16-byte loads (the table and its rows are 16-byte aligned when MP is a
+                // multiple of 4)
+                const int4 *v = reinterpret_cast<const int4 *>(ptr + c0);
 #pragma unroll
-            for (int i = 0; i < SELC; ++i) {
-                const int c = c0 + i;
-                ptv[i] = ptr[c < MP ? c : 0];
+                for (int j = 0; j < SELC / 4; ++j) {
+                    const int4 t = v[j];
+                    ptv[4 * j] = t.x;
+                    ptv[4 * j + 1] = t.y;
+                    ptv[4 * j + 2] = t.z;
+                    ptv[4 * j + 3] = t.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < SELC; ++i) {
+                    const int c = c0 + i;
+                    ptv[i] = ptr[c < MP ? c : 0];
+                }
             }
         }
     }

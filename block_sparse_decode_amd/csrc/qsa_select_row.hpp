@@ -77,10 +77,24 @@ template <int C>
 __device__ __forceinline__ void select_row_load(const float *srow, int MP, uint32_t (&key)[C])
 {
     const int c0 = (threadIdx.x & 63) * C;
+    if (C >= 4 && (MP & 3) == 0 && c0 + C <= MP) {
+        // the lane's columns in 16-byte loads (the row starts 16-byte aligned when MP is a
+        // multiple of 4: the score table itself is)
+        const uint4 *v = reinterpret_cast<const uint4 *>(srow + c0);
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int c = c0 + i;
-        key[i] = __float_as_uint(srow[c < MP ? c : 0]);
+        for (int j = 0; j < C / 4; ++j) {
+            const uint4 t = v[j];
+            key[4 * j] = t.x;
+            key[4 * j + 1] = t.y;
+            key[4 * j + 2] = t.z;
+            key[4 * j + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int c = c0 + i;
+            key[i] = __float_as_uint(srow[c < MP ? c : 0]);
+        }
     }
 }
 
