@@ -710,7 +710,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     // ---- 3. online softmax over this wave's sub-chunks, the next one in flight -----
     const int lc = prm.log2P - 5;                   // log2(sub-chunks per page)
     const int NU = (int)U << lc;
-    const int u_lo = S == 1 ? 0 : (int)(((int64_t)s * NU) / S), u_hi = S == 1 ? NU : (int)(((int64_t)(s + 1) * NU) / S);
+    // (s + 1) * NU <= 64 * 4096 sub-chunks: 32-bit products and the host's divisor for S
+    const int u_lo = S == 1 ? 0 : (int)fast_div((uint32_t)(s * NU), prm.div_splits);
+    const int u_hi = S == 1 ? NU : (int)fast_div((uint32_t)((s + 1) * NU), prm.div_splits);
     // this lane's column's logit scale: sm_scale * k_global * log2(e), times the 2^e its q
     // operand was scaled down by (exact)
     const float c1 = ldexpf(prm.qk_scale_log2, q_col_exp[li]);

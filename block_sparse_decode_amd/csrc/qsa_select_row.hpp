@@ -162,23 +162,31 @@ __device__ __forceinline__ uint64_t select_row_take(uint32_t (&key)[C], int n, i
 
     // 3. ties at T go to the highest pages: rank each tie by the ties at higher pages (later
     //    lanes, then later slots of this lane)
-    uint32_t eq_lane = 0;
-#pragma unroll
-    for (int i = 0; i < C; ++i) eq_lane += (krem != 0u && key[i] == T) ? 1u : 0u;
-    const uint32_t eq_incl = wave_inclusive_scan(eq_lane);
-    uint32_t higher = (uint32_t)__builtin_amdgcn_readlane((int)eq_incl, 63) - eq_incl;
     uint64_t take = 0;                    // bit i: column c0 + i is in the row's selection
+    if (krem == 0u) {
+        // no tie at T: the keys above it (the common case, and the only one after an early
+        // exit of the search)
 #pragma unroll
-    for (int i = C - 1; i >= 0; --i) {
-        const int p = c0 + i;
-        bool t = key[i] > T;
-        if (krem != 0u && key[i] == T) {
-            t = higher < krem;
-            ++higher;
+        for (int i = 0; i < C; ++i) take |= (uint64_t)(key[i] > T) << i;
+    } else {
+        uint32_t eq_lane = 0;
+#pragma unroll
+        for (int i = 0; i < C; ++i) eq_lane += key[i] == T ? 1u : 0u;
+        const uint32_t eq_incl = wave_inclusive_scan(eq_lane);
+        uint32_t higher = (uint32_t)__builtin_amdgcn_readlane((int)eq_incl, 63) - eq_incl;
+#pragma unroll
+        for (int i = C - 1; i >= 0; --i) {
+            bool t = key[i] > T;
+            if (key[i] == T) {
+                t = higher < krem;
+                ++higher;
+            }
+            if (t) take |= 1ull << i;
         }
-        if (p >= wlo && p < n) t = true;  // the window is always kept
-        if (t) take |= 1ull << i;
     }
+    // the window [wlo, n) is always kept: this lane's columns lo .. hi - 1 of it
+    const int lo = min(max(wlo - c0, 0), C), hi = min(max(n - c0, 0), C);
+    take |= ((1ull << hi) - 1ull) & ~((1ull << lo) - 1ull);   // (C <= 32)
 
     return take;
 }
