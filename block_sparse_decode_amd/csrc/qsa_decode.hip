@@ -230,13 +230,16 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
     r.pm = 0u;
     r.phys = 0;
     for (; u < u_hi; u += kDecodeWaves) {
+        // the entry's physical page is read beside its page word, whether or not the unit
+        // turns out visible: one LDS round trip instead of two
         const uint32_t pm = __builtin_amdgcn_readfirstlane(u_pm[u >> lc]);
+        const int32_t ph = __builtin_amdgcn_readfirstlane(u_phys[u >> lc]);
         const int c = u & ((1 << lc) - 1);
         if (c < (int)(pm >> 24)) {
             r.have = true;
             r.c = c;
             r.pm = pm;
-            r.phys = __builtin_amdgcn_readfirstlane(u_phys[u >> lc]);
+            r.phys = ph;
             break;
         }
     }

@@ -109,11 +109,12 @@ __device__ __forceinline__ uint64_t select_row_take(uint32_t (&key)[C], int n, i
     const int c0 = lane * C;
 
     // 1. keys; 0 marks a non-candidate
+    // (class mask 0x007: signaling NaN, quiet NaN, -inf)
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const int p = c0 + i;
         const float s = __uint_as_float(key[i]);
-        key[i] = (p < wlo && !(s != s) && s != -__builtin_inff()) ? float_order_key(s) : 0u;
+        key[i] = (p < wlo && !__builtin_amdgcn_class(s, 0x007)) ? float_order_key(s) : 0u;
     }
     const uint32_t ncand = wave_count_ge<C>(key, 1u);
     QSA_SELECT_STAMP(2);
