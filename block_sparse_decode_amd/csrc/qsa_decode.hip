@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     // A column's running max is raised only when a logit exceeds it by more than this
     // (log2 units), so most sub-chunks skip the rescale; P stays <= 2^8 in f16.
     constexpr float kLazy = 8.0f;
-    static_assert(NDT * 64 * 16 <= 32 * D * 2, "a wave's published tiles must fit its V staging tile");
+    static_assert(NDT * 64 * 16 <= 32 * D * 2, "a wave's O^T tiles must fit its V staging tile");
     static_assert(NDT <= NW, "every output tile needs an owner wave");
     static_assert(SELC <= 32, "a one-row tile's selection mask is kept in 32 bits");
     static_assert(D / 8 <= 16, "one V row holds at most 16 swizzled chunks");
@@ -850,12 +850,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     if (prm.uniform_rows && checker && (ro_check0 != r0 || ro_check1 != r1)) set_error(prm.err, QSA_DEVERR_ROWS);
 
     // ---- 4. merge the waves (fixed order); wave w < d/16 finishes output tile w --------
-    // Every wave publishes its column maxima and denominators, and in its own V staging tile
-    // (which no other wave touches) the O^T tiles that other waves own, packed in ascending
-    // tile order without its own. After one barrier, each wave takes the common column max M
-    // and the weights 2^(m_w - M), and the owner of tile w sums that tile over the waves in
-    // ascending wave order, as every wave sums the denominators, so the result does not
-    // depend on which wave does the sum.
+    // Every wave publishes its column maxima and denominators, and all its O^T tiles in its
+    // own V staging tile (which no other wave touches; d/16 tiles of 64 lanes x 16 bytes fill
+    // it exactly). After one barrier, each wave reads the maxima, the denominators and the
+    // tile it owns from every wave, all loads issued before the first use, takes the common
+    // column max M and the weights 2^(m_w - M), and sums in ascending wave order, as every wave
+    // sums the denominators, so the result does not depend on which wave does the sum. No
+    // branch on the wave index: a wave that owns no tile (d = 64) sums tile 0 and drops it.
     {
         float *pub = reinterpret_cast<float *>(vs);
         if (gq == 0) {
@@ -863,43 +864,30 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
             ml_l[wave][li] = oacc[NDT][0];
         }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            if (dt == wave) continue;
-            const int slot = dt < wave ? dt : dt - 1;
-            *reinterpret_cast<f32x4 *>(pub + (slot * 64 + lane) * 4) = oacc[dt];
-        }
+        for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(pub + (dt * 64 + lane) * 4) = oacc[dt];
     }
     __syncthreads();
     const bool owns_tile = wave < NDT;
-    f32x4 o_own = oacc[0];          // the merged tile `wave` (owner waves only)
+    const int tsel = owns_tile ? wave : 0;
+    float mws[NW], lws[NW];
+    f32x4 ows[NW];
 #pragma unroll
-    for (int dt = 1; dt < NDT; ++dt)
-        if (dt == wave) o_own = oacc[dt];
+    for (int w = 0; w < NW; ++w) {
+        mws[w] = ml_m[w][li];
+        lws[w] = ml_l[w][li];
+        ows[w] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(&vsm[w][0]) + (tsel * 64 + lane) * 4);
+    }
     float M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, ml_m[w][li]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mws[w]);
     float Lsum = 0.0f;
-    {
-        f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    f32x4 o_own = (f32x4){0.f, 0.f, 0.f, 0.f};      // the merged tile `wave` (owner waves only)
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const float mw = ml_m[w][li];
-            const float wgt = (mw == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-            Lsum = __builtin_fmaf(wgt, ml_l[w][li], Lsum);
-            if (owns_tile) {
-                f32x4 o;
-                if (w == wave) {
-                    o = o_own;
-                } else {
-                    const int slot = wave < w ? wave : wave - 1;
-                    o = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(&vsm[w][0]) +
-                                                         (slot * 64 + lane) * 4);
-                }
+    for (int w = 0; w < NW; ++w) {
+        const float wgt = (mws[w] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mws[w] - M);
+        Lsum = __builtin_fmaf(wgt, lws[w], Lsum);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wgt, o[i], acc[i]);
-            }
-        }
-        o_own = acc;
+        for (int i = 0; i < 4; ++i) o_own[i] = __builtin_fmaf(wgt, ows[w][i], o_own[i]);
     }
     m_col = M;
     QSA_STAMP(11);
