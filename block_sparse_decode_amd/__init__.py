@@ -96,7 +96,7 @@ class DecodePlan(ctypes.Structure):
         ("col_tiles", ctypes.c_int32),
         ("splits", ctypes.c_int32),
         ("select_cols", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("waves", ctypes.c_int32),
         ("workgroups", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
     ]

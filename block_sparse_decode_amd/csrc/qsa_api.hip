@@ -124,6 +124,14 @@ int auto_splits(const qsa_shape *sh)
     return (int)s;
 }
 
+// Every tile holds columns of one row only: one row per tile, or 16-column tiles of rows of a
+// multiple of 16 q heads.
+bool one_row_tiles(const qsa_shape *sh)
+{
+    const int G = sh->num_q_heads / sh->num_kv_heads;
+    return G <= 16 ? tile_cols(sh) == G : G % 16 == 0;
+}
+
 int64_t decode_tiles(const qsa_shape *sh)
 {
     return (int64_t)sh->num_requests * sh->num_kv_heads * col_tiles(sh);
@@ -245,6 +253,7 @@ qsa_status qsa_plan_decode(const qsa_shape *sh, int32_t num_splits, int32_t fuse
     plan->splits = splits;
     plan->select_cols = (fused && sh->topk + sh->window > 0) ? fused_select_cols(sh->max_pages) : 0;
     const int64_t items = decode_tiles(sh) * splits;
+    plan->waves = decode_waves(one_row_tiles(sh), (int)std::min<int64_t>(decode_tiles(sh), 1 << 30), splits);
     plan->workgroups = (items + kXcdCount - 1) / kXcdCount * kXcdCount;
     plan->workspace_bytes = decode_ws_bytes(sh, splits);
     return QSA_OK;
@@ -332,10 +341,7 @@ qsa_status decode_call(const qsa_shape *sh, const qsa_paged *pg, const uint16_t 
     prm.gate = gate;
     prm.kv_format = sh->kv_format;
     prm.uniform_rows = (int64_t)sh->num_rows == (int64_t)sh->num_requests * sh->max_rows_per_request;
-    {
-        const int G = sh->num_q_heads / sh->num_kv_heads;
-        prm.one_row_tiles = G <= 16 ? prm.tile_cols == G : G % 16 == 0;
-    }
+    prm.one_row_tiles = one_row_tiles(sh);
     hipError_t e = hipSuccess;
     if (clear_counters && need > 0) {
         e = launch_clear_words(prm.counters, prm.tiles, (hipStream_t)stream);

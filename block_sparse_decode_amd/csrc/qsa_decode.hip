@@ -221,6 +221,7 @@ struct UnitCursor {
     bool have;
 };
 
+template <int NW>
 __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const uint32_t *u_pm,
                                                 const int32_t *u_phys)
 {
@@ -229,7 +230,7 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
     r.c = 0;
     r.pm = 0u;
     r.phys = 0;
-    for (; u < u_hi; u += kDecodeWaves) {
+    for (; u < u_hi; u += NW) {
         // the entry's physical page is read beside its page word, whether or not the unit
         // turns out visible: one LDS round trip instead of two
         const uint32_t pm = __builtin_amdgcn_readfirstlane(u_pm[u >> lc]);
@@ -256,10 +257,10 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
 // Occupancy: LDS allows two workgroups per CU. The one-row form is allowed up to 256
 // registers per lane but takes about 126, so two of its workgroups still fit a CU; the
 // general form is held to 128.
-template <int D, int SELC, int F, bool ONE>
-__global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_kernel(DecodeParams prm)
+template <int D, int SELC, int F, bool ONE, int NWV>
+__global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse_decode_kernel(DecodeParams prm)
 {
-    constexpr int NW = kDecodeWaves;
+    constexpr int NW = NWV;
     constexpr int NT = NW * 64;
     constexpr int KS = D / 32;              // k-steps of S^T = K Q^T
     constexpr int DQ = D / 4;               // elements per lane group
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     // (log2 units), so most sub-chunks skip the rescale; P stays <= 2^8 in f16.
     constexpr float kLazy = 8.0f;
     static_assert(NDT * 64 * 16 <= 32 * D * 2, "a wave's O^T tiles must fit its V staging tile");
-    static_assert(NDT <= NW, "every output tile needs an owner wave");
+    static_assert(NW == kDecodeWaves || (ONE && NW == 4), "4-wave workgroups are built for one-row tiles only");
     static_assert(SELC <= 32, "a one-row tile's selection mask is kept in 32 bits");
     static_assert(D / 8 <= 16, "one V row holds at most 16 swizzled chunks");
 
@@ -837,11 +838,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
         oacc[NDT] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop, oacc[NDT], 0, 0, 0);
     };
 
-    UnitCursor u = seek_unit(u_lo + wave, u_hi, lc, u_pm, u_phys);
+    UnitCursor u = seek_unit<NW>(u_lo + wave, u_hi, lc, u_pm, u_phys);
     if (u.have) load_unit<D, F>(prm, u.phys, g, u.c, lco, lso, kr, vr);
     QSA_STAMP(8);
     while (u.have) {
-        const UnitCursor un = seek_unit(u.u + NW, u_hi, lc, u_pm, u_phys);
+        const UnitCursor un = seek_unit<NW>(u.u + NW, u_hi, lc, u_pm, u_phys);
         process(u, un, kr, vr);
         u = un;
     }
@@ -849,14 +850,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
     // (the offsets loaded at the start have long arrived; before any early return of a split)
     if (prm.uniform_rows && checker && (ro_check0 != r0 || ro_check1 != r1)) set_error(prm.err, QSA_DEVERR_ROWS);
 
-    // ---- 4. merge the waves (fixed order); wave w < d/16 finishes output tile w --------
+    // ---- 4. merge the waves (fixed order); wave w finishes output tiles w, w + NW, ... ----
     // Every wave publishes its column maxima and denominators, and all its O^T tiles in its
     // own V staging tile (which no other wave touches; d/16 tiles of 64 lanes x 16 bytes fill
     // it exactly). After one barrier, each wave reads the maxima, the denominators and the
-    // tile it owns from every wave, all loads issued before the first use, takes the common
+    // tiles it owns from every wave, all loads issued before the first use, takes the common
     // column max M and the weights 2^(m_w - M), and sums in ascending wave order, as every wave
     // sums the denominators, so the result does not depend on which wave does the sum. No
-    // branch on the wave index: a wave that owns no tile (d = 64) sums tile 0 and drops it.
+    // branch on the wave index: a wave that owns fewer tiles sums tile 0 in their place and
+    // drops it.
+    constexpr int TPW = (NDT + NW - 1) / NW;        // output tiles per wave
     {
         float *pub = reinterpret_cast<float *>(vs);
         if (gq == 0) {
@@ -867,32 +870,42 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
         for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4 *>(pub + (dt * 64 + lane) * 4) = oacc[dt];
     }
     __syncthreads();
-    const bool owns_tile = wave < NDT;
-    const int tsel = owns_tile ? wave : 0;
+    int own[TPW];                                    // the tiles this wave finishes (< NDT: owned)
+#pragma unroll
+    for (int ot = 0; ot < TPW; ++ot) own[ot] = wave + ot * NW;
     float mws[NW], lws[NW];
-    f32x4 ows[NW];
+    f32x4 ows[TPW][NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         mws[w] = ml_m[w][li];
         lws[w] = ml_l[w][li];
-        ows[w] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(&vsm[w][0]) + (tsel * 64 + lane) * 4);
+#pragma unroll
+        for (int ot = 0; ot < TPW; ++ot) {
+            const int tsel = own[ot] < NDT ? own[ot] : 0;
+            ows[ot][w] = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(&vsm[w][0]) +
+                                                          (tsel * 64 + lane) * 4);
+        }
     }
     float M = NEG_INF;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, mws[w]);
     float Lsum = 0.0f;
-    f32x4 o_own = (f32x4){0.f, 0.f, 0.f, 0.f};      // the merged tile `wave` (owner waves only)
+    f32x4 o_own[TPW];                                // the merged tiles own[ot] (owned ones only)
+#pragma unroll
+    for (int ot = 0; ot < TPW; ++ot) o_own[ot] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         const float wgt = (mws[w] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mws[w] - M);
         Lsum = __builtin_fmaf(wgt, lws[w], Lsum);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o_own[i] = __builtin_fmaf(wgt, ows[w][i], o_own[i]);
+        for (int ot = 0; ot < TPW; ++ot)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o_own[ot][i] = __builtin_fmaf(wgt, ows[ot][w][i], o_own[ot][i]);
     }
     m_col = M;
     QSA_STAMP(11);
     if (S > 1) {
-        // Publish this split's partial (each owner its tile, wave 0 the denominators and the
+        // Publish this split's partial (each owner its tiles, wave 0 the denominators and the
         // column maxima), count it, and let the tile's last split merge. The partial moves
         // through agent-scope (coherent) stores and loads: each such access is coherent
         // across the XCDs' L2s on its own, so the handoff needs only the stores' completion
@@ -902,11 +915,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
         constexpr int kOff = (NDT + 1) * 64 * 4;
         float *tile_part = prm.part + (int64_t)tile * S * PF;
         float *mine = tile_part + (int64_t)s * PF;
-        if (owns_tile) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __hip_atomic_store(mine + (wave * 4 + i) * 64 + lane, o_own[i], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        for (int ot = 0; ot < TPW; ++ot) {
+            if (own[ot] < NDT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __hip_atomic_store(mine + (own[ot] * 4 + i) * 64 + lane, o_own[ot][i], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         if (wave == 0) {
             __hip_atomic_store(mine + (NDT * 4) * 64 + lane, Lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -923,55 +939,61 @@ __global__ __launch_bounds__(kDecodeWaves * 64, ONE ? 2 : 4) void sparse_decode_
         __syncthreads();
         if (scan_tmp[1] != (uint32_t)(S - 1)) return;
         // the last split: every partial's stores completed before its count. Each wave merges
-        // the partials (its owned tile, the denominators, the maxima) in ascending split order
+        // the partials (its owned tiles, the denominators, the maxima) in ascending split order
         // with a running max, eight splits at a time: a group's loads, its own partial's
         // included, all issue before the first is used (clamped, unconditional), so a group
         // costs one round trip. With at most eight splits this is one group and the plain
-        // weighted sum with the common max.
+        // weighted sum with the common max. A wave with two tiles merges them one after the
+        // other, each the same way, so the denominators and maxima come out the same.
         constexpr int kGroup = 8;
-        const int tsel = owns_tile ? wave : 0;
-        float Ms = NEG_INF, Ls = 0.0f;
-        f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-        for (int sp0 = 0; sp0 < S; sp0 += kGroup) {
-            float mv[kGroup], lv[kGroup];
-            f32x4 ov[kGroup];
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                const float *part = tile_part + (int64_t)min(sp0 + i, S - 1) * PF;
-                mv[i] = __hip_atomic_load(part + kOff + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                lv[i] = __hip_atomic_load(part + (NDT * 4) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int ot = 0; ot < TPW; ++ot) {
+            const int tsel = own[ot] < NDT ? own[ot] : 0;
+            float Ms = NEG_INF, Ls = 0.0f;
+            f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int sp0 = 0; sp0 < S; sp0 += kGroup) {
+                float mv[kGroup], lv[kGroup];
+                f32x4 ov[kGroup];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ov[i][e] = __hip_atomic_load(part + (tsel * 4 + e) * 64 + lane, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+                for (int i = 0; i < kGroup; ++i) {
+                    const float *part = tile_part + (int64_t)min(sp0 + i, S - 1) * PF;
+                    mv[i] = __hip_atomic_load(part + kOff + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    lv[i] = __hip_atomic_load(part + (NDT * 4) * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ov[i][e] = __hip_atomic_load(part + (tsel * 4 + e) * 64 + lane, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                }
+                float cm = Ms;
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i)
+                    if (sp0 + i < S) cm = fmaxf(cm, mv[i]);
+                const float resc = (Ms == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(Ms - cm);
+                Ls *= resc;
+                acc *= resc;
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) {
+                    const float wgt = (sp0 + i >= S || mv[i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mv[i] - cm);
+                    Ls = __builtin_fmaf(wgt, lv[i], Ls);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wgt, ov[i][e], acc[e]);
+                }
+                Ms = cm;
             }
-            float cm = Ms;
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i)
-                if (sp0 + i < S) cm = fmaxf(cm, mv[i]);
-            const float resc = (Ms == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(Ms - cm);
-            Ls *= resc;
-            acc *= resc;
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                const float wgt = (sp0 + i >= S || mv[i] == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(mv[i] - cm);
-                Ls = __builtin_fmaf(wgt, lv[i], Ls);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wgt, ov[i][e], acc[e]);
-            }
-            Ms = cm;
+            o_own[ot] = acc;
+            Lsum = Ls;
+            m_col = Ms;
         }
-        o_own = acc;
-        Lsum = Ls;
-        m_col = Ms;
         if (wave == 0 && lane == 0) __hip_atomic_store(prm.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (!colv) return;
     const int row = r0 + jc, head = g * G + (col - jc * G);
     const float sc = (Lsum > 0.0f) ? prm.v_global / Lsum : 0.0f;
-    if (owns_tile) {
-        const int dt = wave;
-        f32x4 o = o_own * sc;
+#pragma unroll
+    for (int ot = 0; ot < TPW; ++ot) {
+        if (own[ot] >= NDT) continue;
+        const int dt = own[ot];
+        f32x4 o = o_own[ot] * sc;
         if (prm.gate) {
             // the gated epilogue: out * sigmoid(gate), one rounding to bf16 after the product
             const uint2 gr = *reinterpret_cast<const uint2 *>(prm.gate + ((int64_t)row * prm.Hq + head) * D +
@@ -997,16 +1019,21 @@ static hipError_t launch_decode_d(const DecodeParams &prm, hipStream_t stream)
     const int64_t per = ((int64_t)prm.tiles * prm.splits + kXcds - 1) / kXcds;   // work items per XCD
     const unsigned grid = (unsigned)(per * kXcds);
     const bool fp8 = prm.kv_format == kFp8;
-    if (prm.one_row_tiles) {
+    if (prm.one_row_tiles && decode_waves(prm.one_row_tiles, prm.tiles, prm.splits) == 4) {
         if (fp8)
-            sparse_decode_kernel<D, SELC, kFp8, true><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+            sparse_decode_kernel<D, SELC, kFp8, true, 4><<<grid, 4 * 64, 0, stream>>>(prm);
         else
-            sparse_decode_kernel<D, SELC, kNvfp4, true><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+            sparse_decode_kernel<D, SELC, kNvfp4, true, 4><<<grid, 4 * 64, 0, stream>>>(prm);
+    } else if (prm.one_row_tiles) {
+        if (fp8)
+            sparse_decode_kernel<D, SELC, kFp8, true, kDecodeWaves><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+        else
+            sparse_decode_kernel<D, SELC, kNvfp4, true, kDecodeWaves><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
     } else {
         if (fp8)
-            sparse_decode_kernel<D, SELC, kFp8, false><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+            sparse_decode_kernel<D, SELC, kFp8, false, kDecodeWaves><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
         else
-            sparse_decode_kernel<D, SELC, kNvfp4, false><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
+            sparse_decode_kernel<D, SELC, kNvfp4, false, kDecodeWaves><<<grid, kDecodeWaves * 64, 0, stream>>>(prm);
     }
     return hipGetLastError();
 }

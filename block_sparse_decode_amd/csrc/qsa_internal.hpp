@@ -149,6 +149,16 @@ hipError_t launch_step_slots(const SlotParams &prm, int B, hipStream_t stream);
 // number of waves per decode workgroup
 constexpr int kDecodeWaves = 8;
 
+// Waves per workgroup of an attention launch. An 8-wave one-row workgroup takes half a CU
+// (its V staging fills half the LDS), so a launch of more than two work items per CU runs
+// in rounds, the last of them part-filled. One-row tiles then take 4-wave workgroups, three
+// of which fit a CU, and the items run together in fewer rounds.
+constexpr int kDecodeCUs = 256;
+constexpr int decode_waves(int one_row_tiles, int tiles, int splits)
+{
+    return one_row_tiles && (int64_t)tiles * splits > 2 * kDecodeCUs ? 4 : kDecodeWaves;
+}
+
 // XCDs of the chip; decode workgroups are numbered so that each XCD takes a contiguous run of
 // work items (the grid is rounded up to a multiple of this)
 constexpr int kXcdCount = 8;

@@ -84,8 +84,8 @@ def run(workload: str, launches: int = 200, fused: bool = True, groups: int = 0)
     t0 = a[:, :, 0][live].min()
     rel = (a - t0) * 0.01                       # 100 MHz ticks -> microseconds
     kind = "fused selection + attention" if fused else "attention (selection given)"
-    print(f"workload {workload}: {kind}, {n} workgroups ({plan.rows_per_tile} row(s) per tile, "
-          f"{plan.splits} split(s)), traced launch mean {us:.2f} us over {launches} back-to-back launches")
+    print(f"workload {workload}: {kind}, {n} workgroups of {plan.waves} waves ({plan.rows_per_tile} row(s) per "
+          f"tile, {plan.splits} split(s)), traced launch mean {us:.2f} us over {launches} back-to-back launches")
     print(f"{'point':18s} {'p10':>7s} {'p50':>7s} {'p90':>7s} {'max':>7s}   (us from the first workgroup's entry)")
     # a stamp belongs to this launch when it is not older than its wave's entry (workgroups of
     # split tiles that are not the last to finish leave the later points of an earlier launch)

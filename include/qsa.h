@@ -172,6 +172,9 @@ size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
  *   splits          KV splits per tile (as qsa_sparse_decode resolves num_splits)
  *   select_cols     score columns per lane of the fused selection (2, 4, 8 or 16), 0 when
  *                   not fused or when max_pages > 1024 (a separate selection launch runs first)
+ *   waves           waves per attention workgroup: 8, or 4 when the tiles hold one row each
+ *                   and tiles x splits exceed two per CU (three 4-wave workgroups fit a CU,
+ *                   two 8-wave ones)
  *   workgroups      attention workgroups launched
  *   workspace_bytes qsa_workspace_bytes(shape, num_splits)
  * QSA_ERR_INVALID_ARG for a NULL plan, negative num_splits or an invalid shape.
@@ -182,7 +185,7 @@ typedef struct qsa_decode_plan {
     int32_t col_tiles;
     int32_t splits;
     int32_t select_cols;
-    int32_t reserved;
+    int32_t waves;
     int64_t workgroups;
     size_t  workspace_bytes;
 } qsa_decode_plan;

@@ -323,24 +323,31 @@ int main(void) {
     assert got == [ctypes.sizeof(D), D.select_cols.offset, D.workgroups.offset, D.workspace_bytes.offset]
 
 
-@pytest.mark.parametrize("B,R,Hq,Hkv,MP,rows,cols,ctiles", [
-    (16, 4, 32, 4, 512, 1, 8, 4),      # the 32K verify workload: 256 one-row tiles
-    (32, 4, 32, 4, 64, 2, 16, 2),      # 2 rows x 8 q heads: 256 tiles
-    (64, 4, 16, 4, 64, 4, 16, 1),      # 4 rows x 4 q heads: 256 tiles
-    (64, 3, 20, 4, 64, 3, 15, 1),      # 3 rows x 5 q heads
-    (8, 4, 16, 4, 64, 1, 4, 4),        # few tiles: rows halved down to one
-    (8, 2, 48, 2, 64, 0, 16, 3),       # 24 q heads per KV head: tiles cut rows
-    # verify rows over 1024-page tables share few pages: 768 one-row tiles (3 rounds of the
-    # CUs) beat 384 two-row ones (2 rounds of tiles with twice the union)
-    (48, 4, 32, 4, 1024, 1, 8, 4),
+@pytest.mark.parametrize("B,R,Hq,Hkv,MP,rows,cols,ctiles,waves", [
+    (16, 4, 32, 4, 512, 1, 8, 4, 8),      # the 32K verify workload: 256 one-row tiles
+    (32, 4, 32, 4, 64, 2, 16, 2, 8),      # 2 rows x 8 q heads: 256 tiles
+    (64, 4, 16, 4, 64, 4, 16, 1, 8),      # 4 rows x 4 q heads: 256 tiles
+    (64, 3, 20, 4, 64, 3, 15, 1, 8),      # 3 rows x 5 q heads
+    (8, 4, 16, 4, 64, 1, 4, 4, 8),        # few tiles: rows halved down to one
+    (8, 2, 48, 2, 64, 0, 16, 3, 8),       # 24 q heads per KV head: tiles cut rows
+    # verify rows over 1024-page tables share few pages: 768 one-row tiles beat 384 two-row
+    # ones (2 rounds of tiles with twice the union); 768 one-row tiles take 4-wave workgroups
+    (48, 4, 32, 4, 1024, 1, 8, 4, 4),
+    (16, 2, 64, 4, 256, 1, 16, 2, 8),     # 16-column tiles of 16-head rows: one row each, 128
+    (64, 4, 64, 4, 256, 1, 16, 4, 4),     # the same over 1024 tiles
     # a context step's neighbouring rows over 128 pages share most of theirs: two rows per tile
-    (4, 256, 32, 4, 128, 2, 16, 128),
+    (4, 256, 32, 4, 128, 2, 16, 128, 8),
 ])
-def test_plan_tile_heights(B, R, Hq, Hkv, MP, rows, cols, ctiles):
+def test_plan_tile_heights(B, R, Hq, Hkv, MP, rows, cols, ctiles, waves):
     sh = _shape(num_requests=B, num_rows=B * R, max_rows_per_request=R, num_q_heads=Hq, num_kv_heads=Hkv,
                 max_pages=MP)
     p = q.qsa_plan_decode(sh, 0, True)
     assert (p.rows_per_tile, p.tile_cols, p.col_tiles) == (rows, cols, ctiles)
+    assert p.waves == waves
+    # forced splits count too: more than two work items per CU take 4-wave one-row workgroups
+    p3 = q.qsa_plan_decode(sh, 3, True)
+    one_row = rows == 1 or (rows == 0 and Hq // Hkv % 16 == 0)
+    assert p3.waves == (4 if one_row and B * Hkv * ctiles * 3 > 512 else 8)
     assert p.workspace_bytes == q.qsa_workspace_bytes(sh, 0)
     assert p.workgroups % 8 == 0 and p.workgroups >= B * Hkv * ctiles * p.splits
     assert p.select_cols == (2 if MP <= 128 else 4 if MP <= 256 else 8 if MP <= 512 else 16)
