@@ -44,23 +44,43 @@
 #include "qsa_internal.hpp"
 
 // A traced build (-DQSA_TRACE) records, per wave of the first kTraceGroups workgroups of each
-// launch, the 100 MHz real-time clock at the points of the kernel named in trace_points
-// (a lane-0 vector store per point); qsa_trace_read copies them to the host. The normal
-// build has neither the stamps nor the buffer.
+// launch, the 100 MHz real-time clock at the points of the kernel named in trace_points;
+// qsa_trace_read copies them to the host. Lane 0 of each wave keeps its stamps in LDS and
+// copies them to the global buffer when the wave leaves: a global store per stamp would
+// count in the wave's vector-memory counter, and every later wait for a load would then
+// also wait for the stores to be acknowledged. The normal build has neither the stamps nor
+// the buffers.
 #if defined(QSA_TRACE)
 namespace qsa {
 constexpr int kTraceGroups = 4096, kTracePoints = 16;
 __device__ unsigned long long qsa_trace_stamps[kTraceGroups * 8 * kTracePoints];
+__shared__ unsigned long long qsa_trace_lds[8][kTracePoints];
+__device__ __forceinline__ void trace_clear()
+{
+    const unsigned t = threadIdx.x;
+    if ((t & 63u) == 0u)
+        for (int k = 0; k < kTracePoints; ++k) qsa_trace_lds[t >> 6][k] = 0ull;
+}
 __device__ __forceinline__ void trace_stamp(int k)
 {
     const unsigned t = threadIdx.x;
+    if ((t & 63u) == 0u) qsa_trace_lds[t >> 6][k] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void trace_flush()
+{
+    const unsigned t = threadIdx.x;
     if ((t & 63u) == 0u && blockIdx.x < (unsigned)kTraceGroups)
-        qsa_trace_stamps[((size_t)blockIdx.x * 8 + (t >> 6)) * kTracePoints + k] = __builtin_amdgcn_s_memrealtime();
+        for (int k = 0; k < kTracePoints; ++k)
+            qsa_trace_stamps[((size_t)blockIdx.x * 8 + (t >> 6)) * kTracePoints + k] = qsa_trace_lds[t >> 6][k];
 }
 }  // namespace qsa
 #define QSA_STAMP(k) qsa::trace_stamp(k)
+#define QSA_TRACE_BEGIN() qsa::trace_clear()
+#define QSA_TRACE_END() qsa::trace_flush()
 #else
 #define QSA_STAMP(k) ((void)0)
+#define QSA_TRACE_BEGIN() ((void)0)
+#define QSA_TRACE_END() ((void)0)
 #endif
 #define QSA_SELECT_STAMP(k) QSA_STAMP(k)
 
@@ -307,6 +327,7 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
     const uint32_t wg = blockIdx.x;
     const uint32_t item = (wg % kXcds) * per + wg / kXcds;
     if (item >= n_items) return;
+    QSA_TRACE_BEGIN();
     QSA_STAMP(0);
     const int tile = (int)fast_div(item, prm.div_splits), s = (int)item - tile * S;
     const int T = prm.col_tiles;
@@ -340,7 +361,10 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
     const int G = (int)prm.div_group.d;
     const int TW = prm.tile_cols;   // this tile: columns col0 .. col0 + TW - 1 of the request's R x G
     const int col0 = ct * TW;
-    if (col0 >= R * G) return;
+    if (col0 >= R * G) {
+        QSA_TRACE_END();
+        return;
+    }
     const int j_lo = (int)fast_div((uint32_t)col0, prm.div_group);
     const int j_hi = min(R - 1, (int)fast_div((uint32_t)(col0 + TW - 1), prm.div_group));
     const int nrow = j_hi - j_lo + 1;                // rows of this tile (<= 4)
@@ -937,7 +961,10 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
             if (lane == 0) scan_tmp[1] = done;
         }
         __syncthreads();
-        if (scan_tmp[1] != (uint32_t)(S - 1)) return;
+        if (scan_tmp[1] != (uint32_t)(S - 1)) {
+            QSA_TRACE_END();
+            return;
+        }
         // the last split: every partial's stores completed before its count. Each wave merges
         // the partials (its owned tiles, the denominators, the maxima) in ascending split order
         // with a running max, eight splits at a time: a group's loads, its own partial's
@@ -986,6 +1013,7 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
         }
         if (wave == 0 && lane == 0) __hip_atomic_store(prm.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    QSA_TRACE_END();
     if (!colv) return;
     const int row = r0 + jc, head = g * G + (col - jc * G);
     const float sc = (Lsum > 0.0f) ? prm.v_global / Lsum : 0.0f;
@@ -1011,6 +1039,7 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
     if (wave == 0 && gq == 0 && prm.lse)
         prm.lse[(int64_t)row * prm.Hq + head] = (Lsum > 0.0f) ? (m_col + __log2f(Lsum)) * 0.69314718055994531f : NEG_INF;
     QSA_STAMP(10);
+    QSA_TRACE_END();
 }
 
 template <int D, int SELC>

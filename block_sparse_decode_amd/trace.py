@@ -6,8 +6,10 @@ prints their distribution over the workgroups of one launch.
     python -m block_sparse_decode_amd.trace run [--workload W]    # on the GPU
 
 Times are microseconds from the earliest workgroup's entry. The traced library is built into
-_build/ and loaded in place of libqsa.so; a stamp waits for the LDS and scalar operations in
-flight before it, so the traced kernel runs slightly slower than the product build.
+_build/ and loaded in place of libqsa.so. A wave keeps its stamps in LDS and writes them out when
+it leaves, so the stamps add no stores for later loads to wait behind; a stamp still waits for
+the LDS and scalar operations in flight before it, so the traced kernel runs slightly slower
+than the product build.
 """
 from __future__ import annotations
 
@@ -91,9 +93,15 @@ def run(workload: str, launches: int = 200, fused: bool = True, groups: int = 0)
     # split tiles that are not the last to finish leave the later points of an earlier launch)
     entry = a[:, :, 0:1]
     for k, (name, who) in NAMES.items():
-        sl = slice(None) if who is None else slice(who, who + 1)
-        v = rel[:, sl, k]
-        ok = (a[:, sl, k] > 0) & (a[:, sl, k] >= entry[:, sl, 0])
+        if who is None:
+            v = rel[:, :, k]
+            ok = (a[:, :, k] > 0) & (a[:, :, k] >= entry[:, :, 0])
+        else:
+            # stamped by the selecting wave alone (which wave that is may vary by workgroup)
+            sw = np.argmax(a[:, :, k], axis=1)
+            rows = np.arange(a.shape[0])
+            v = rel[rows, sw, k]
+            ok = (a[rows, sw, k] > 0) & (a[rows, sw, k] >= entry[rows, sw, 0])
         v = v[ok]
         if v.size == 0:
             continue
