@@ -233,7 +233,7 @@ __device__ __forceinline__ int vswz(int row) { return ((row << 1) + ((row >> 2) 
 
 // A wave's position in its split's range of sub-chunks. Sub-chunk u is sub-chunk
 // u mod (P/32) of union entry u / (P/32); sub-chunks that no row of the tile can see (past
-// the longest row's length) are skipped.
+// the longest row's length), and those of an entry without a valid physical page, are skipped.
 struct UnitCursor {
     int u, c;
     uint32_t pm;
@@ -256,7 +256,7 @@ __device__ __forceinline__ UnitCursor seek_unit(int u, int u_hi, int lc, const u
         const uint32_t pm = __builtin_amdgcn_readfirstlane(u_pm[u >> lc]);
         const int32_t ph = __builtin_amdgcn_readfirstlane(u_phys[u >> lc]);
         const int c = u & ((1 << lc) - 1);
-        if (c < (int)(pm >> 24)) {
+        if (c < (int)(pm >> 24) && ph >= 0) {        // (an entry without a valid page holds -1)
             r.have = true;
             r.c = c;
             r.pm = pm;
@@ -378,11 +378,12 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
     // thread marks its entries' pages in the bitmap, and after a second one wave 0 lists the
     // marked pages. The last wave converts q into the MFMA B operand in LDS before the first
     // barrier. Union order: ascending page, as for one-row tiles.
-    // A one-row tile with the selection fused in takes a shorter way: its selecting wave
-    // holds the page-table entries of its columns in registers beside the score keys and
-    // writes the union itself (the selected pages with a valid physical page, ascending, as
-    // the union build would list them), so neither the LDS copy of the page table nor the
-    // union build and its barrier are needed.
+    // A one-row tile with the selection fused in takes a shorter way: wave 1 copies the
+    // page-table entries of the row's columns into LDS while the selecting wave selects, and
+    // after the barrier every thread places its share of the selected pages (ascending) in
+    // the union, so neither the bitmap nor the union build and its barrier are needed. One-row
+    // unions keep a selected page without a valid physical page in its place, with -1 for its
+    // physical page, and the loop skips its sub-chunks.
     const int nwords = ((MP + 3) / 4 + 3) & ~3;
     uint32_t *bm = reinterpret_cast<uint32_t *>(lds_area);
     int32_t *pt_row = reinterpret_cast<int32_t *>(bm + nwords);
@@ -417,31 +418,27 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
     } else {
         if (wave < nrow) select_row_load<SELC>(prm.scores + (int64_t)(r0 + j_lo + wave) * MP, MP, skey);
     }
-    // one-row tiles: the page-table entries of the selecting lane's columns
-    int ptv[SELC > 0 ? SELC : 1];
-    if constexpr (SELC > 0) {
-        if (one_row && wave == 0) {
-            // as the score loads: one clamped load per column, no branch; only selected
-            // columns, all inside the row, are read
+    // One-row tiles with the selection fused in: wave 1 copies the page-table entries of the
+    // row's columns into LDS (one_pt, in the selecting wave's column order), so that the
+    // selecting wave waits for its score row alone. The entries of the selected columns are
+    // read after the barrier.
+    if constexpr (one_row) {
+        if (wave == 1) {
             const int c0 = lane * SELC;
             const int32_t *ptr = prm.page_table + (int64_t)b * MP;
             if (SELC >= 4 && (MP & 3) == 0 && c0 + SELC <= MP) {
                 // 16-byte loads (the table and its rows are 16-byte aligned when MP is a
                 // multiple of 4)
                 const int4 *v = reinterpret_cast<const int4 *>(ptr + c0);
+                int4 *d = reinterpret_cast<int4 *>(one_pt + c0);
 #pragma unroll
-                for (int j = 0; j < SELC / 4; ++j) {
-                    const int4 t = v[j];
-                    ptv[4 * j] = t.x;
-                    ptv[4 * j + 1] = t.y;
-                    ptv[4 * j + 2] = t.z;
-                    ptv[4 * j + 3] = t.w;
-                }
+                for (int j = 0; j < SELC / 4; ++j) d[j] = v[j];
             } else {
+                // one clamped load per column; columns past the row are never selected
 #pragma unroll
                 for (int i = 0; i < SELC; ++i) {
                     const int c = c0 + i;
-                    ptv[i] = ptr[c < MP ? c : 0];
+                    one_pt[c] = ptr[c < MP ? c : 0];
                 }
             }
         }
@@ -468,12 +465,13 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
     }
     if constexpr (lean_one) {
         if (wave == 0) {
-            // The row's listed pages, deduplicated and in ascending order (the order the fused
-            // selection lists them in), with a valid physical page. Each listed visible page's
-            // page-table entry is loaded at once (one dependent round trip for all of them);
-            // valid pages set their bit in a bitmap over the table and store their physical
-            // page beside it; the set bits, read back in ascending order with a prefix count
-            // for the positions, are the union. Wave 0 alone, so no workgroup barrier.
+            // The row's listed visible pages, deduplicated and in ascending order (the order the
+            // fused selection lists them in). Each one's page-table entry is loaded at once (one
+            // dependent round trip for all of them); the pages set their bit in a bitmap over the
+            // table and store their physical page beside it; the set bits, read back in ascending
+            // order with a prefix count for the positions, are the union. A page without a valid
+            // physical page keeps its place with -1 for it, as in the fused selection, so both
+            // calls give their waves the same sub-chunks. Wave 0 alone, so no workgroup barrier.
             const RowGeom geo = row_geom(Lb, Rb, j_lo, prm.log2P, MP);
             uint32_t *okmap = reinterpret_cast<uint32_t *>(lds_area);          // kMaxPages bits
             int32_t *phys_of = reinterpret_cast<int32_t *>(okmap + kMaxPages / 32);
@@ -497,11 +495,8 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
                     continue;
                 }
                 const int ph = phv[i];
-                if (p < 0 || p >= geo.pages || ph == -1) continue;
-                if ((uint32_t)ph >= npc) {
-                    set_error(prm.err, QSA_DEVERR_PAGE_ID);
-                    continue;
-                }
+                if (p < 0 || p >= geo.pages) continue;
+                if (ph != -1 && (uint32_t)ph >= npc) set_error(prm.err, QSA_DEVERR_PAGE_ID);
                 phys_of[p] = ph;                          // duplicates store the same value
                 atomicOr(&okmap[p >> 5], 1u << (p & 31));
             }
@@ -527,7 +522,8 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
                     const int vis = lenc - (p << prm.log2P);
                     const int nc = vis >= P ? P / 32 : (vis + 31) / 32;
                     u_pm[pos] = (uint32_t)p | (1u << 16) | ((uint32_t)nc << 24);
-                    u_phys[pos] = phys_of[p];
+                    const int32_t ph = phys_of[p];
+                    u_phys[pos] = (uint32_t)ph < npc ? ph : -1;
                     ++pos;
                 }
             }
@@ -537,36 +533,20 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
     if constexpr (SELC > 0) {
         if constexpr (one_row) {
             if (wave == 0) {
-                // The row's selection and its union (the selected pages whose page-table entry
-                // is a valid physical page) are placed by the whole workgroup after the
-                // barrier: a single wave placing every column itself would take hundreds of
-                // instructions while seven waves wait. This wave publishes, per lane, its
-                // columns' selection and union masks, their prefix counts over the lanes (one
-                // scan: selection count in the low half, union count in the high half) and the
-                // columns' page-table entries.
+                // The row's selection is placed by the whole workgroup after the barrier: a
+                // single wave placing every column itself would take hundreds of instructions
+                // while the other waves wait. This wave publishes, per lane, its columns'
+                // selection mask and its prefix count over the lanes.
                 const RowGeom geo = row_geom(Lb, Rb, j_lo, prm.log2P, MP);
                 const uint32_t take = (uint32_t)select_row_take<SELC>(skey, geo.pages, prm.k, prm.W);
                 QSA_STAMP(4);
-                const uint32_t npc = prm.NP < ((int64_t)1 << 31) ? (uint32_t)prm.NP : 0x80000000u;
-                uint32_t ok = 0u, bad = 0u;
-#pragma unroll
-                for (int i = 0; i < SELC; ++i) {
-                    const uint32_t valid = (uint32_t)((uint32_t)ptv[i] < npc);
-                    const uint32_t invalid = (uint32_t)(ptv[i] != -1) & (valid ^ 1u);
-                    ok |= valid << i;
-                    bad |= invalid << i;
-                }
-                ok &= take;
-                if (bad & take) set_error(prm.err, QSA_DEVERR_PAGE_ID);
-                const uint32_t cnt = (uint32_t)__builtin_popcount(take) | ((uint32_t)__builtin_popcount(ok) << 16);
+                const uint32_t cnt = (uint32_t)__builtin_popcount(take);
                 const uint32_t incl = wave_inclusive_scan(cnt);
-                one_pub[lane] = take | (ok << 16);
+                one_pub[lane] = take;
                 one_pub[64 + lane] = incl - cnt;
-#pragma unroll
-                for (int i = 0; i < SELC; ++i) one_pt[lane * SELC + i] = ptv[i];
                 if (lane == 63) {
-                    scan_tmp[0] = incl >> 16;
-                    scan_tmp[1] = incl & 0xffffu;
+                    scan_tmp[0] = incl;          // union entries: the selected pages
+                    scan_tmp[1] = incl;          // selection length
                 }
                 QSA_STAMP(5);
             }
@@ -619,21 +599,27 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
     __syncthreads();
     QSA_STAMP(7);
     if constexpr (one_row) {
-        // every thread places up to two of the row's columns (64 * SELC <= 1024) in the
-        // selection row (ascending, in wave 0's V staging tile) and in the union
+        // every thread places up to four of the row's columns (64 * SELC <= 1024) in the
+        // selection row (ascending, in wave 0's V staging tile) and in the union. The union
+        // lists every selected page at the same position; a page without a valid physical page
+        // has -1 for it (the loop skips its sub-chunks), and one outside the pool also sets the
+        // error.
         const int lenc = (int)min(row_geom(Lb, Rb, j_lo, prm.log2P, MP).len, (int64_t)MP << prm.log2P);
+        const uint32_t npc = prm.NP < ((int64_t)1 << 31) ? (uint32_t)prm.NP : 0x80000000u;
         int32_t *sel_row = reinterpret_cast<int32_t *>(lds_area);
         for (int c = tid; c < 64 * SELC; c += NT) {
             const int ol = c / SELC, i = c % SELC;
-            const uint32_t pub = one_pub[ol], ex = one_pub[64 + ol];
-            const uint32_t tk = pub & 0xffffu, okm = pub >> 16, below = (1u << i) - 1u;
-            if ((tk >> i) & 1u) sel_row[(ex & 0xffffu) + (uint32_t)__builtin_popcount(tk & below)] = c;
-            if ((okm >> i) & 1u) {
-                const int upos = (int)((ex >> 16) + (uint32_t)__builtin_popcount(okm & below));
+            const uint32_t tk = one_pub[ol];
+            if ((tk >> i) & 1u) {
+                const int pos = (int)(one_pub[64 + ol] + (uint32_t)__builtin_popcount(tk & ((1u << i) - 1u)));
+                sel_row[pos] = c;
                 const int vis = lenc - (c << prm.log2P);
                 const int nc = vis >= P ? P / 32 : (vis + 31) / 32;
-                u_pm[upos] = (uint32_t)c | (1u << 16) | ((uint32_t)nc << 24);
-                u_phys[upos] = one_pt[c];
+                u_pm[pos] = (uint32_t)c | (1u << 16) | ((uint32_t)nc << 24);
+                const int32_t ph = one_pt[c];
+                const bool valid = (uint32_t)ph < npc;
+                if (!valid && ph != -1) set_error(prm.err, QSA_DEVERR_PAGE_ID);
+                u_phys[pos] = valid ? ph : -1;
             }
         }
         __syncthreads();
