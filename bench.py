@@ -195,7 +195,8 @@ def attention_flop(w, selected):
 
 def fused_kernel_name(w):
     """Name rocprofv3 gives the fused selection + attention kernel for this workload, from the
-    launch plan the library reports (selection columns per lane, one-row tiles)."""
+    launch plan the library reports (selection columns per lane, one-row tiles, waves per
+    workgroup)."""
     import block_sparse_decode_amd as q
     from block_sparse_decode_amd.batch import DeviceBatch
     c = w.cfg
@@ -205,7 +206,8 @@ def fused_kernel_name(w):
     plan = q.qsa_plan_decode(sh, 0, True)
     G = c.q_heads // c.kv_heads
     one = plan.tile_cols == G if G <= 16 else G % 16 == 0
-    return f"sparse_decode_kernel<{c.head_dim}, {plan.select_cols}, {fmt}, {'true' if one else 'false'}>"
+    return (f"sparse_decode_kernel<{c.head_dim}, {plan.select_cols}, {fmt}, {'true' if one else 'false'}, "
+            f"{plan.waves}>")
 
 
 def _cpu_model():
