@@ -607,9 +607,19 @@ __global__ __launch_bounds__(NWV * 64, ONE ? (NWV == 4 ? 3 : 2) : 4) void sparse
         const int lenc = (int)min(row_geom(Lb, Rb, j_lo, prm.log2P, MP).len, (int64_t)MP << prm.log2P);
         const uint32_t npc = prm.NP < ((int64_t)1 << 31) ? (uint32_t)prm.NP : 0x80000000u;
         int32_t *sel_row = reinterpret_cast<int32_t *>(lds_area);
-        for (int c = tid; c < 64 * SELC; c += NT) {
-            const int ol = c / SELC, i = c % SELC;
-            const uint32_t tk = one_pub[ol];
+        // a fixed number of columns per thread, so that all their mask reads issue before the
+        // first is used (one LDS round trip for them, one more for the few selected ones)
+        constexpr int kPlace = (64 * SELC + NT - 1) / NT;
+        uint32_t tks[kPlace];
+#pragma unroll
+        for (int k = 0; k < kPlace; ++k) {
+            const int c = tid + k * NT;
+            tks[k] = c < 64 * SELC ? one_pub[c / SELC] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < kPlace; ++k) {
+            const int c = tid + k * NT, ol = c / SELC, i = c % SELC;
+            const uint32_t tk = tks[k];
             if ((tk >> i) & 1u) {
                 const int pos = (int)(one_pub[64 + ol] + (uint32_t)__builtin_popcount(tk & ((1u << i) - 1u)));
                 sel_row[pos] = c;
