@@ -137,3 +137,34 @@ def test_wide_grid_gated(splits):
     torch.cuda.synchronize()
     assert np.array_equal(st.selected.cpu().numpy(), sel_ref)
     _check(st.out, st.lse, ref_out, ref_lse, f"gated splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [0, 2])
+@pytest.mark.parametrize("idx", [0, 6])
+def test_wide_grid_fused_equals_composed_and_repeats(idx, splits):
+    """With 4-wave workgroups the fused call (selection in the prologue, union placed by every
+    thread) and the composed one (selection given, union built by one wave) list the same union
+    entries, a selected page without a valid physical page included, so their waves stream the
+    same sub-chunks in the same order: out and lse agree bit for bit. Repeated launches of each
+    call give the same bits."""
+    cfg = CASES[idx]
+    w, ref_s, ref_sel, _ = _case(cfg)
+    b = DeviceBatch.upload(w)
+    assert q.qsa_plan_decode(b.shape(), splits, True).waves == 4
+    ref = Step(b, num_splits=splits, fused=False)
+    fus = Step(b, num_splits=splits, fused=True)
+    for st in (ref, fus):
+        st.scores.copy_(torch.from_numpy(ref_s).cuda())
+    ref.select_call()
+    ref.decode_call()
+    fus.select_decode_call()
+    torch.cuda.synchronize()
+    assert np.array_equal(fus.selected.cpu().numpy(), ref_sel)
+    assert torch.equal(fus.out, ref.out) and torch.equal(fus.lse, ref.lse)
+    first_out, first_lse = fus.out.clone(), fus.lse.clone()
+    for _ in range(5):
+        fus.select_decode_call()
+        ref.decode_call()
+    torch.cuda.synchronize()
+    assert torch.equal(fus.out, first_out) and torch.equal(fus.lse, first_lse)
+    assert torch.equal(ref.out, first_out) and torch.equal(ref.lse, first_lse)
