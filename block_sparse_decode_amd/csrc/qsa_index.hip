@@ -9,9 +9,9 @@
 // arithmetic must be reproducible bit for bit. It therefore runs on the plain ALUs, never
 // on MFMA, whose internal summation order is not specified. A workgroup covers 64 pages of
 // one query row; each lane owns one page and holds that page's key for the current KV head
-// in VGPRs: as raw bf16 pairs, converted to fp32 one 16-element chunk at a time when one pass
-// covers all of the KV head's q heads (at most 8), else kept whole as fp32 for the later
-// passes. Each wave takes KV heads in turn, eight of the KV head's q heads per pass. q is wave-uniform, so it reaches the lanes through the cross-lane operand network
+// in VGPRs: as raw bf16 pairs, loaded a few 16-element chunks ahead and converted to fp32 one
+// chunk at a time when one pass covers all of the KV head's q heads (at most 8), else kept
+// whole as fp32 for the later passes. Each wave takes KV heads in turn, eight of the KV head's q heads per pass. q is wave-uniform, so it reaches the lanes through the cross-lane operand network
 // rather than through per-element LDS reads: a VGPR holds 16 consecutive elements of one
 // head, element m in lane m of every 16-lane row, and each v_fmac_f32 reads its q operand
 // through DPP row_newbcast, which hands one lane's value to its whole row. Each head's sum
@@ -28,6 +28,13 @@ namespace qsa {
 constexpr int kIndexWaves = 4;
 constexpr int kIndexCUs = 256;
 constexpr int kHeadGroup = 8;        // q heads per pass
+// One-pass form: key chunks in registers at once, and the waves per SIMD the compiler is asked
+// to allow (its registers: 67 per lane at d = 128, so seven waves fit a SIMD). Measured against
+// the whole key in registers (115 per lane, four waves): 32K verify 8.9 -> 8.4 us, context step
+// 22.2 -> 21.0 us, 131K 8.9 -> 8.5 us, the others unchanged; a ring of one chunk (eight waves)
+// lost 0.7 us on the wide mixed batch.
+constexpr int kRing = 2;
+constexpr int kOnePassWaves = 6;
 
 // acc[t] = fma(q_t[16c + n], k[16c + n], acc[t]) for n = 0 .. 15 in order and t = 0 .. 7:
 // operand 8 + t holds q_t[16c + m] in lane m of each 16-lane row, and row_newbcast:n gives
@@ -55,11 +62,11 @@ __device__ __forceinline__ void fmac16x8(float (&a)[kHeadGroup], const float (&q
 // NW waves per workgroup, each taking KV heads wave, wave + NW, ...: 4 by default; 8 when the
 // grid is small and there are at least 8 KV heads, so that the KV heads of a (row, page tile)
 // spread over more SIMDs. ONEG: at most 8 q heads per KV head, so one pass covers them all and
-// the key is converted to fp32 one 16-element chunk at a time instead of being kept whole;
-// that halves the VGPRs, and a large grid then holds four waves per SIMD instead of two, so
-// one wave's loads overlap another's fmas.
+// the key is converted to fp32 one 16-element chunk at a time instead of being kept whole,
+// and it is loaded as it is used, kRing chunks ahead; that cuts the VGPRs to a third, and a
+// grid then holds up to seven waves per SIMD, so one wave's loads overlap others' fmas.
 template <int D, int NW, bool ONEG>
-__global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams prm)
+__global__ __launch_bounds__(NW * 64, ONEG ? kOnePassWaves : 2) void index_scores_kernel(IndexParams prm)
 {
     constexpr int HG = kHeadGroup;
     __shared__ float red[NW][kWave];
@@ -167,10 +174,13 @@ __global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams pr
             uint32_t qu[HG];
             load_q(g, 0, qu);
             const uint4 *kp = reinterpret_cast<const uint4 *>(prm.keys + ((int64_t)(cand ? phys : 0) * prm.Hkv + g) * D);
-            uint4 kraw[D / 8];
+            // the key in a ring of kRing 16-element chunks (two 16-byte loads each): the first
+            // kRing chunks load now, and chunk c + kRing loads into chunk c's registers once
+            // chunk c is converted, so a wave holds a fraction of the key and a SIMD more waves
+            uint4 kraw[2 * kRing];
 #pragma unroll
-            for (int c = 0; c < D / 8; ++c) kraw[c] = kp[c];
-            __builtin_amdgcn_sched_barrier(0);    // keep every key load ahead of the wait for q
+            for (int c = 0; c < 2 * kRing; ++c) kraw[c] = kp[c];
+            __builtin_amdgcn_sched_barrier(0);    // keep these key loads ahead of the wait for q
             // q as fp32: element e of head t at [(e / 16) * 16 + e % 16][t]
             if (lane < D / 2) {
                 float4 *dst = reinterpret_cast<float4 *>(qf + 2 * lane * HG);
@@ -199,12 +209,17 @@ __global__ __launch_bounds__(NW * 64, 2) void index_scores_kernel(IndexParams pr
                 __builtin_amdgcn_sched_barrier(0);    // the next chunk's reads stay ahead of these fmas
                 const float qc[HG] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
                 float kk[16];
+                const int slot = c % kRing;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const uint4 v = kraw[2 * c + h];
+                    const uint4 v = kraw[2 * slot + h];
                     float *k8 = &kk[8 * h];
                     k8[0] = bf16lo(v.x); k8[1] = bf16hi(v.x); k8[2] = bf16lo(v.y); k8[3] = bf16hi(v.y);
                     k8[4] = bf16lo(v.z); k8[5] = bf16hi(v.z); k8[6] = bf16lo(v.w); k8[7] = bf16hi(v.w);
+                }
+                if (c + kRing < NC) {
+                    kraw[2 * slot] = kp[2 * (c + kRing)];
+                    kraw[2 * slot + 1] = kp[2 * (c + kRing) + 1];
                 }
                 fmac16x8(a, qc, kk);
             }
