@@ -14,7 +14,10 @@
 //     register slot and a scalar popcount, exact in any order. The search starts at the
 //     highest bit in which the candidates differ (the bits above it are common to all of
 //     them, so T has them too), and stops early when exactly k keys are >= the prefix:
-//     those k keys are then the top k, with no tie across the boundary.
+//     those k keys are then the top k, with no tie across the boundary. A search still
+//     running after kRederiveStep steps (in practice a row with several keys equal to the
+//     k-th) takes the common bits of the keys left in its interval in one step the same way,
+//     and ends there when they are all equal.
 //  3. Keys above T are all taken. Of the keys equal to T, the highest page indices fill
 //     the remaining slots, ranked by a wave suffix count of ties.
 //  4. The union with the window is compacted in ascending page order by a wave prefix
@@ -30,6 +33,12 @@
 #endif
 
 namespace qsa {
+
+// Bit steps after which a search still running re-derives its interval's common bits (see
+// select_row_take): on the workloads' score tables only rows with several keys equal to the
+// k-th get that far (their search otherwise takes every remaining bit of that value, 27 steps
+// on the 32K verify workload against at most 18 for the other rows).
+constexpr int kRederiveStep = 16;
 
 // Keys of the whole wave at or above t (wave-uniform): one ballot per register slot, all
 // compares of a group of (up to) 8 slots issued before the first scalar popcount reads a mask,
@@ -146,11 +155,53 @@ __device__ __forceinline__ uint64_t select_row_take(uint32_t (&key)[C], int n, i
         // the loop state stays scalar: `left` counts the bits still to decide
         int left = hb + 1;
         uint32_t bitv = hb >= 0 ? 1u << hb : 0u;
-        for (; left > 0; --left, bitv >>= 1) {
+        // at most kRederiveStep steps, then (a search still running) one re-derivation and the
+        // remaining steps; `left` > 0 after a loop means it stopped at exactly k keys
+        const int stop = left > kRederiveStep ? left - kRederiveStep : 0;
+        bool exact = false;
+        for (; left > stop; --left, bitv >>= 1) {
             const uint32_t t = T | bitv;
             const uint32_t c = wave_count_ge<C>(key, t);
             if (c >= k) T = t;
-            if (c == k) break;
+            if (c == k) {
+                exact = true;
+                break;
+            }
+        }
+        if (!exact && left > 0) {
+            // A row still searching here almost always has several keys equal to the k-th (no
+            // prefix leaves exactly k keys at or above it), and the search would go on through
+            // every remaining bit of that value. The k-th key lies in the interval
+            // [T, T + 2 bitv): every key at or above T + 2 bitv is one of fewer than k, and at
+            // least k are at or above T. So the bits in which the interval's keys agree are the
+            // k-th key's, and the search restarts below the highest bit in which they differ,
+            // as it started below the candidates' common bits (both counts stay as they were).
+            // When they all agree the k-th key is their value.
+            uint32_t iand = 0xffffffffu, ior = 0u;
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                const bool in = key[i] != 0u && key[i] >= T && ((key[i] - T) >> 1) < bitv;
+                iand &= in ? key[i] : 0xffffffffu;
+                ior |= in ? key[i] : 0u;
+            }
+            iand = wave_bitreduce<false>(iand);
+            ior = wave_bitreduce<true>(ior);
+            const uint32_t d = iand ^ ior;
+            if (d == 0u) {
+                T = iand;
+                left = 0;
+            } else {
+                const int hb2 = 31 - __builtin_clz(d);
+                T = iand & ~((2u << hb2) - 1u);
+                left = hb2 + 1;
+                bitv = 1u << hb2;
+            }
+            for (; left > 0; --left, bitv >>= 1) {
+                const uint32_t t = T | bitv;
+                const uint32_t c = wave_count_ge<C>(key, t);
+                if (c >= k) T = t;
+                if (c == k) break;
+            }
         }
         if (left > 0) {
             T -= 1u;                      // the k keys >= the prefix are exactly the keys > T

@@ -185,6 +185,67 @@ def test_fused_selection_on_injected_tie_heavy_scores(rows, context, k, W, split
     _check_attention(_u16(fus.out), fus.lse.cpu().numpy(), ref_out, ref_lse, "fused ties")
 
 
+def _cluster_scores(rng, N, MP, k, spread):
+    """Rows whose k-th place falls in a cluster of values at most `spread` ulps apart (repeats
+    included), above a spread of lower values and below fewer than k clearly larger ones: the
+    bit search runs past its re-derivation step, where the interval's keys are all equal
+    (spread 1) or still differ in their low bits (the search then restarts below them)."""
+    s = (rng.standard_normal((N, MP)) - 3.0).astype(np.float32)
+    for r in range(N):
+        nb = int(rng.integers(k // 2, k))
+        cols = rng.permutation(MP)
+        s[r, cols[:nb]] = 10.0 + rng.random(nb).astype(np.float32)
+        nc = int(rng.integers(k - nb + 1, k - nb + 12))
+        x0 = np.float32(rng.uniform(0.5, 4.0))
+        m = rng.integers(0, spread, size=nc)
+        s[r, cols[nb:nb + nc]] = (x0.view(np.int32) + m).astype(np.int32).view(np.float32)
+    return s
+
+
+@pytest.mark.parametrize("spread", [1, 4, 64, 4096])
+def test_selection_on_clustered_scores(spread):
+    """The k-th place inside a cluster of nearly equal scores: long bit searches, through the
+    re-derivation of the interval's common bits, against the oracle row by row."""
+    rng = np.random.default_rng(100 + spread)
+    B, R, P, MP, k, W = 40, 4, 64, 1000, 32, 2
+    seq = np.full(B, MP * P, np.int32)
+    ro = (np.arange(B + 1) * R).astype(np.int32)
+    N = B * R
+    scores = _cluster_scores(rng, N, MP, k, spread)
+    ref = oracle.select(seq, ro, P, MP, k, W, scores)
+    sh = q.Shape(B, N, R, 1, 1, 64, P, MP, 1, k, W, 1.0)
+    seq_d, ro_d, sc_d = (torch.from_numpy(a).cuda() for a in (seq, ro, scores))
+    pg = q.Paged(None, seq_d.data_ptr(), ro_d.data_ptr(), None, None, None, None, None, 1.0, 1.0, None)
+    sel = torch.empty((N, k + W), dtype=torch.int32, device="cuda")
+    q.qsa_select_topk(sh, pg, sc_d, sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("spread", [1, 16])
+def test_fused_selection_on_clustered_scores(spread):
+    """The same score tables through the selection fused into the attention launch: the
+    oracle's rows, and bit for bit the composed calls' outputs."""
+    cfg = synth.Config("fused_cluster", 6, 4, 8, 2, 64, 64, (40000, 60000), 32, 2, seed=331 + spread)
+    w = workload(cfg)
+    b = DeviceBatch.upload(w)
+    scores = _cluster_scores(np.random.default_rng(7 + spread), w.N, w.MP, 32, spread)
+    print(f"[fused cluster] MP={w.MP} spread={spread}", flush=True)
+    ref = Step(b, fused=False)
+    fus = Step(b, fused=True)
+    for st in (ref, fus):
+        st.scores.copy_(torch.from_numpy(scores).cuda())
+    ref.select_call()
+    ref.decode_call()
+    fus.selected.fill_(-7)
+    fus.select_decode_call()
+    torch.cuda.synchronize()
+    ref_sel = oracle.select_w(w, scores)
+    assert np.array_equal(ref.selected.cpu().numpy(), ref_sel)
+    assert np.array_equal(fus.selected.cpu().numpy(), ref_sel)
+    assert torch.equal(fus.out, ref.out) and torch.equal(fus.lse, ref.lse)
+
+
 def test_selection_repeated_launch_determinism():
     """The same rows launched 50 times select identical sets in identical order."""
     w = workload("mtp_verify_32k")
