@@ -40,17 +40,27 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_decode_{workload}.
 DECODE_SOURCES = ("qsa_api.hip", "qsa_decode.hip", "qsa_device.hpp", "qsa_internal.hpp", "qsa_select_row.hpp")
 
 
+def _strip_comments(text):
+    """C/C++ source without its comments and with each run of white space made one space (string
+    and character literals kept as they are), so that the hash below follows the code the
+    compiler sees, not the prose and layout around it."""
+    import re
+    tok = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+    code = tok.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), text)
+    return " ".join(code.split())
+
+
 def kernel_source_hash():
-    """SHA-256 over the sources of the fused kernel and the header; traffic counters are valid
-    for this hash only."""
+    """SHA-256 over the sources of the fused kernel and the header, comments and layout removed;
+    traffic counters are valid for this hash only."""
     import hashlib
     h = hashlib.sha256()
     files = [os.path.join(ROOT, "block_sparse_decode_amd", "csrc", f) for f in DECODE_SOURCES] + \
         [os.path.join(ROOT, "include", "qsa.h")]
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_strip_comments(fh.read()).encode())
     return h.hexdigest()
 
 
@@ -357,7 +367,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "requests are independent, so a deployment shards them across GPUs with no exchange", file=sys.stderr)
         sys.exit(2)
 

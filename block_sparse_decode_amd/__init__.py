@@ -129,7 +129,7 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise FileNotFoundError(
-                f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+                f"{LIB_PATH} is missing: build it first (python -m block_sparse_decode_amd.build)")
         L = ctypes.CDLL(LIB_PATH)
         P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         sp, pp = ctypes.POINTER(Shape), ctypes.POINTER(Paged)

@@ -1,10 +1,11 @@
 // qsa_decode.hip -- split-KV sparse GQA attention over NVFP4 (or FP8) pages, with LSE merge.
 //
-// Method: TensorRT-LLM PR #20937, Description > What changes: NVFP4 sparse GQA decode as a
-// split-K + merge kernel with a lean one-split variant, a request-grouped verify kernel with
-// a per-row merge and a gated epilogue, and a row-tile pass for context and mixed steps.
-// PR #20276, "What runs on the fast paths": K/V tiles are read once per group of rows of one
-// request.
+// Method: TensorRT-LLM PR #20937, Description > What changes: the NVFP4 sparse GQA decode
+// splits a tile's pages over workgroups and merges their partial softmax results, with a
+// cheaper form when one split suffices; verify rows are grouped by request and merged per row,
+// with an optional gate on the output; context and mixed steps run as tiles of rows.
+// PR #20276, "What runs on the fast paths": the rows of one request that share K/V pages read
+// them together.
 //
 // Work item: a tile is (request b, KV head g, a run of at most 16 of the request's R x G
 // query columns, whole rows when G <= 16); each tile is split S ways, one 8-wave workgroup

@@ -2,7 +2,7 @@
 //
 // Formats (OCP specs): e2m1 elements (1 sign, 2 exponent bits with bias 1, 1 mantissa bit),
 // E4M3FN block scales (bias 7, NaN at S.1111.111, no infinities), bf16 queries and keys.
-// The NVFP4 KV cache of the pages stores "uint8 e2m1 pages + e4m3 block scales"
+// The pages' NVFP4 KV cache keeps the e2m1 elements as uint8 codes beside e4m3 block scales
 // (TensorRT-LLM PR #20276, Features, NVFP4 KV cache row).
 #pragma once
 

@@ -88,7 +88,7 @@ typedef struct qsa_shape {
 
 /*
  * The paged KV cache. One physical page index addresses every plane (PR #20276, Features,
- * NVFP4 KV cache: the data and scale pools keep one page index). Device memory.
+ * NVFP4 KV cache: codes and scales share the page numbering). Device memory.
  *   page_table  int32 [B][MP]           logical page -> physical page, -1 = no page
  *   seq_lens    int32 [B]               tokens of request b, including this step's rows
  *   row_offsets int32 [B+1]             rows of request b are [row_offsets[b], row_offsets[b+1])
@@ -164,8 +164,8 @@ size_t qsa_workspace_bytes(const qsa_shape *shape, int32_t num_splits);
  * The launch the attention calls make for this shape (host only; nothing is launched).
  * A tile is a run of at most 16 of one request's query columns (its rows x the G q heads of
  * one KV head, row-major); every page any of its rows selected is read once for the tile
- * (PR #20276, Performance > What runs on the fast paths: K/V tiles read once per group of
- * rows). `fused` != 0 describes qsa_select_sparse_decode, 0 qsa_sparse_decode.
+ * (PR #20276, Performance > What runs on the fast paths: rows of a request share their K/V
+ * page reads). `fused` != 0 describes qsa_select_sparse_decode, 0 qsa_sparse_decode.
  *   tile_cols       query columns per tile (1..16)
  *   rows_per_tile   whole rows per tile (tile_cols / G) when G <= 16; 0 when tiles cut rows
  *   col_tiles       tiles per (request, KV head)
@@ -194,8 +194,8 @@ qsa_status qsa_plan_decode(const qsa_shape *shape, int32_t num_splits, int32_t f
 
 /*
  * Split-KV sparse GQA attention over the selected pages, with an LSE merge (PR #20937,
- * What changes: a split-K + merge decode kernel with a lean one-split variant;
- * request-grouped verify attention with a per-row merge).
+ * What changes: the decode kernel splits the pages and merges the partial results, with a
+ * cheaper form for one split; verify rows are grouped by request and merged per row).
  *   q          bf16  [N][Hq][d]     (device)
  *   selected   int32 [N][k + W]     (device; entries outside [0, MP) are ignored, and
  *                                    a page listed twice counts once)
@@ -226,7 +226,7 @@ qsa_status qsa_sparse_decode(const qsa_shape *shape, const qsa_paged *paged,
 
 /*
  * The selection fused into the attention (PR #20276, Performance > What runs on the fast
- * paths: the block top-k fused with its expansion to tokens; Decisions worth knowing: the
+ * paths: the block top-k runs in the same kernel that turns blocks into tokens; Decisions worth knowing: the
  * fast path produces the canonical rows from one launch). Takes the index scores instead
  * of the selection rows and writes both results: `selected` exactly as qsa_select_topk
  * writes it and `out` / `lse` exactly as qsa_sparse_decode computes them from it, in one

@@ -2,8 +2,8 @@
 
 A tile is a run of at most 16 of a request's query columns (rows x the q heads of one KV
 head); the pages any of its rows selected are read once for the whole tile (TensorRT-LLM
-PR #20276, Performance > What runs on the fast paths: K/V tiles read once per group of
-rows). The launch groups rows only when the batch still gives at least one tile per CU,
+PR #20276, Performance > What runs on the fast paths: rows of a request share their K/V
+page reads). The launch groups rows only when the batch still gives at least one tile per CU,
 so these shapes are large batches of short requests: 2, 3 and 4 rows per tile, and tiles
 that cut rows (24 q heads per KV head). Each case asserts the tile height the launch takes
 (qsa_plan_decode), then compares every (row, head) of `out` and `lse` with the oracle, for
