@@ -194,3 +194,46 @@ def test_workspace_reused_by_a_larger_batch():
         _check(st.out.cpu().numpy().view(np.uint16), st.lse.cpu().numpy(), ref_out, ref_lse,
                f"B={w.B} splits={sp}")
         assert int(ws[:32768].count_nonzero().item()) == 0, "counters left non-zero"
+
+
+@pytest.mark.parametrize("spread", [1, 16])
+def test_grouped_tiles_clustered_scores(spread):
+    """4-row tiles whose rows' k-th place falls in a cluster of nearly equal scores (at most
+    `spread` ulps apart, repeats included): each of the tile's selecting waves runs a long bit
+    search through the re-derivation of its interval's common bits. Selection rows and every
+    output against the oracle, fused and composed."""
+    cfg, rows = CASES[0]
+    w = _workload(cfg)
+    b = DeviceBatch.upload(w)
+    assert q.qsa_plan_decode(b.shape(), 1, True).rows_per_tile == rows
+    rng = np.random.default_rng(40 + spread)
+    k = w.cfg.topk
+    scores = oracle.index_scores(w).copy()
+    for r in range(w.N):
+        cand = np.flatnonzero(np.isfinite(scores[r]))
+        if len(cand) <= k:
+            continue
+        vals = (rng.standard_normal(len(cand)) - 3.0).astype(np.float32)
+        order = rng.permutation(len(cand))
+        nb = int(rng.integers(k // 2, k))
+        vals[order[:nb]] = 10.0 + rng.random(nb).astype(np.float32)
+        nc = min(int(rng.integers(k - nb + 1, k - nb + 6)), len(cand) - nb)
+        x0 = np.float32(rng.uniform(0.5, 4.0))
+        m = rng.integers(0, spread, size=nc)
+        vals[order[nb:nb + nc]] = (x0.view(np.int32) + m).astype(np.int32).view(np.float32)
+        scores[r, cand] = vals
+    ref_sel = oracle.select_w(w, scores)
+    ref_out, ref_lse = _oracle_attention(w, ref_sel)
+    for fused in (True, False):
+        st = Step(b, num_splits=1, fused=fused)
+        st.scores.copy_(torch.from_numpy(scores).cuda())
+        st.selected.fill_(-7)
+        if fused:
+            st.select_decode_call()
+        else:
+            st.select_call()
+            st.decode_call()
+        torch.cuda.synchronize()
+        assert np.array_equal(st.selected.cpu().numpy(), ref_sel)
+        _check(st.out.cpu().numpy().view(np.uint16), st.lse.cpu().numpy(), ref_out, ref_lse,
+               f"{cfg.name} clustered spread={spread} fused={fused}")
