@@ -8,16 +8,18 @@
 // them together.
 //
 // Work item: a tile is (request b, KV head g, a run of at most 16 of the request's R x G
-// query columns, whole rows when G <= 16); each tile is split S ways, one 8-wave workgroup
-// per (tile, split). The host picks the rows per tile and S (see tile_cols and auto_splits
-// in qsa_api.hip): rows are grouped only while that still leaves a tile per CU, since
-// splitting a tile's pages instead costs a merge.
+// query columns, whole rows when G <= 16); each tile is split S ways, one workgroup per
+// (tile, split): 8 waves, or 4 for one-row tiles when there are more than two work items per
+// CU (three such workgroups fit a CU, so the launch runs in one round). The host picks the
+// rows per tile and S (see tile_cols and auto_splits in qsa_api.hip): rows are grouped only
+// while that still leaves a tile per CU, since splitting a tile's pages instead costs a merge.
 //  1. The tile's rows (at most 4 causal rows: verify rows, or a run of a context step's
 //     rows) each list their selected pages (computed here from the scores, one wave per
 //     row, when the selection is fused in). The workgroup builds the union of those pages in
 //     ascending order, each with a row bitmask, in LDS, and drops entries whose page-table
 //     entry is -1. Each page of the union is read once for all the tile's rows. A one-row
-//     tile with the selection fused in has its selecting wave publish the union directly.
+//     tile with the selection fused in has its selecting wave publish the union directly
+//     (in a 4-wave launch after loading only the row's visible score columns).
 //  2. The union's 32-token sub-chunks are numbered page-major. Split s takes a contiguous
 //     range of them and its waves deal that range round-robin, so waves differ by at most
 //     one sub-chunk. Each wave runs an online softmax over its sub-chunks:
