@@ -2,9 +2,9 @@
 // step's rows overwrite are gathered into a stash before the step and written back for the
 // rejected rows afterwards; and the (page, slot) each step row occupies.
 //
-// Method: TensorRT-LLM PR #20937, Description > What changes > Rollback and PLE (a batched
-// rollback of the QSA index planes) and its file list (a rollback gather / restore
-// operation); the placement of a step row is the KV store's (the token at position
+// Method: TensorRT-LLM PR #20937, Description > What changes > Rollback and PLE (the index
+// planes' writes of rejected rows undone in one batch) and its file list (a gather and a
+// restore operation for that rollback); the placement of a step row is the KV store's (the token at position
 // L - R + j of its request).
 //
 // Design: pure data movement, a few hundred bytes per (row, plane). One 64-lane workgroup

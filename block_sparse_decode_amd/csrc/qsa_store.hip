@@ -3,8 +3,8 @@
 // received them recomputed.
 //
 // Method: TensorRT-LLM PR #20276, Performance > What runs on the fast paths (the decode
-// prologue covers index store and compression); PR #20937, Description > What changes (a
-// fused decode prologue over NVFP4 KV); PR #20276, Features, NVFP4 KV cache row (e2m1 codes
+// prologue covers index store and compression); PR #20937, Description > What changes (the
+// prologue that writes a decode step's NVFP4 KV, fused); PR #20276, Features, NVFP4 KV cache row (e2m1 codes
 // and e4m3 block scales in parallel planes addressed by one page id). The pages fix neither
 // the encoder's rounding nor the index compression; the definitions taken here:
 //   placement  row j of a request with R rows and L tokens is the token at position

@@ -259,8 +259,8 @@ qsa_status qsa_select_sparse_decode_static(const qsa_shape *shape, const qsa_pag
 
 /*
  * The KV-store prologue of a step (PR #20276, Performance > What runs on the fast paths:
- * the decode prologue's index store and compression; PR #20937, What changes: a fused
- * decode prologue over NVFP4 KV). Writes this step's new tokens into the paged cache and
+ * the decode prologue's index store and compression; PR #20937, What changes: the prologue
+ * that writes the NVFP4 KV of a decode step, fused). Writes this step's new tokens into the paged cache and
  * recomputes the index keys of the pages that received them.
  *   new_k, new_v  bf16 [N][Hkv][d]  (device): row j of request b (R_b rows) is the token at
  *                 position seq_lens[b] - R_b + j, i.e. page (pos / P), slot (pos % P)
@@ -283,8 +283,8 @@ qsa_status qsa_kv_store(const qsa_shape *shape, const qsa_paged *paged,
                         const uint16_t *new_k, const uint16_t *new_v, void *stream);
 
 /*
- * Index-plane rollback (PR #20937, Description > What changes > Rollback and PLE: a batched
- * rollback of the QSA index planes; its rollback gather / restore operation). Before a
+ * Index-plane rollback (PR #20937, Description > What changes > Rollback and PLE: the index
+ * planes' writes of rejected rows undone in one batch, by a gather and a restore operation). Before a
  * verify step stores its draft rows, qsa_rollback_gather saves the plane rows those rows
  * will overwrite; after acceptance, qsa_rollback_restore writes the saved bytes back for the
  * rejected rows. Kept rows, and every other byte, stay as the step left them.

@@ -402,7 +402,7 @@ void oracle_attention_one(int B, const int32_t *seq_lens, const int32_t *row_off
 /*
  * The KV-store prologue of a decode / verify step [PR20276, Performance > What runs on
  * the fast paths: the decode prologue covers index store and compression; PR20937, What
- * changes: a fused decode prologue over NVFP4 KV]: this step's new K and V tokens are
+ * changes: the prologue that writes a decode step's NVFP4 KV, fused]: this step's new K and V tokens are
  * quantised into their page slots, and the index key of every page that received a token
  * is recomputed. The pages fix neither the encoder's rounding nor the index compression;
  * this file takes these readings:

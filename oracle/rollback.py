@@ -3,8 +3,8 @@
 TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this module. The product path never calls it.
 
-Method: TensorRT-LLM PR #20937, Description > What changes > Rollback and PLE (a batched
-rollback of the QSA index planes) and its file list (a rollback gather/restore operation
+Method: TensorRT-LLM PR #20937, Description > What changes > Rollback and PLE (the index
+planes' writes of rejected rows undone in one batch) and its file list (a gather/restore operation
 whose test restores the rejected rows and leaves the kept rows as the step wrote them).
 The pages give the operation, not its addressing. The reading taken here:
 
