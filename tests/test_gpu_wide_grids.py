@@ -168,3 +168,35 @@ def test_wide_grid_fused_equals_composed_and_repeats(idx, splits):
     torch.cuda.synchronize()
     assert torch.equal(fus.out, first_out) and torch.equal(fus.lse, first_lse)
     assert torch.equal(ref.out, first_out) and torch.equal(ref.lse, first_lse)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_wide_grid_short_long_and_bad_ids(fused):
+    """4-wave launches (which load the request length before the score row and copy only the
+    row's visible columns) on requests whose length is 0 (the row sees nothing), longer than the
+    page table covers (rows clipped, flagged), and a page-table entry past the pool in a row's
+    window (treated as -1, flagged): scores, selection rows and every output against the oracle."""
+    import dataclasses
+    cfg = CASES[0]
+    w0, _, _, _ = _case(cfg)
+    w = dataclasses.replace(w0)
+    w.seq_lens = w0.seq_lens.copy()
+    w.page_table = w0.page_table.copy()
+    P = cfg.page_size
+    w.seq_lens[3] = 0
+    w.seq_lens[7] = w.MP * P + 5
+    n9 = -(-int(w.seq_lens[9]) // P)
+    w.page_table[9, n9 - 1] = w.NP + 3
+    b = DeviceBatch.upload(w)
+    assert q.qsa_plan_decode(b.shape(), 0, fused).waves == 4
+    st = Step(b, fused=fused)
+    st()
+    torch.cuda.synchronize()
+    ref_s = oracle.index_scores(w)
+    assert np.array_equal(st.scores.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+    sel = st.selected.cpu().numpy()
+    assert np.array_equal(sel, oracle.select_w(w, ref_s))
+    ref_out, ref_lse = oracle.attention(w, sel)
+    _check(st.out, st.lse, ref_out, ref_lse, f"short/long/bad fused={fused}")
+    err = int(b.error_word[0].item())
+    assert err & q.QSA_DEVERR_PAGE_ID and err & q.QSA_DEVERR_SEQ_LEN
