@@ -65,7 +65,9 @@ __device__ __forceinline__ void fmac16x8(float (&a)[kHeadGroup], const float (&q
 // the key is converted to fp32 one 16-element chunk at a time instead of being kept whole,
 // and it is loaded as it is used, kRing chunks ahead; that cuts the VGPRs to a third, and a
 // grid then holds up to seven waves per SIMD, so one wave's loads overlap others' fmas.
-template <int D, int NW, bool ONEG>
+// ORD: the dispatch order of a grid whose rows have more than one aligned group of 8 tiles
+// (below).
+template <int D, int NW, bool ONEG, bool ORD>
 __global__ __launch_bounds__(NW * 64, ONEG ? kOnePassWaves : 2) void index_scores_kernel(IndexParams prm)
 {
     constexpr int HG = kHeadGroup;
@@ -88,11 +90,28 @@ __global__ __launch_bounds__(NW * 64, ONEG ? kOnePassWaves : 2) void index_score
     // group of 8 (a partial last group is left as it is): a bijection of the row's tiles that
     // spreads the live ones over the XCDs and keeps the rows of one (request, tile) on one
     // XCD, where they share the tile's keys.
-    const int j = blockIdx.y, b = blockIdx.z;
-    const int x = blockIdx.x;
+    // The dispatcher also starts workgroups in linear-id order, and with the tile fastest
+    // the tiles past short requests' pages are spread over the whole dispatch, each holding
+    // a slot for the round trip of its request's length while live tiles wait. With ORD (a
+    // multiple of 8 tiles per row, more than 8) the linear id is taken apart anew: its value
+    // mod 8 (the XCD) stays the tile's position in its group, and the tile group becomes the
+    // slowest index, so that every request's first group of tiles starts before any second
+    // group, and the groups past short requests come last. Each (tile, row, request) still
+    // runs on the same XCD; the map is a bijection of the grid.
     // (the tile count from MP, an argument already in registers: gridDim would be read from
     // the dispatch packet, one more scalar-cache miss ahead of the page-table load)
     const int tiles_per_row = (prm.MP + kWave - 1) / kWave;
+    int j = blockIdx.y, b = blockIdx.z, x = blockIdx.x;
+    if constexpr (ORD) {
+        // grid (tiles_per_row, rmax, B), tiles_per_row = 8m: id = x + tiles * (j + rmax * b);
+        // id mod 8 = x mod 8, and id / 8 = group * (rmax * B) + (j + rmax * b) afterwards
+        const int RB = prm.rmax * (int)gridDim.z;
+        const int lin = x + tiles_per_row * (j + prm.rmax * b);
+        const int slot = lin >> 3, grp = slot / RB, rem = slot - grp * RB;
+        b = rem / prm.rmax;
+        j = rem - b * prm.rmax;
+        x = grp * 8 + (lin & 7);
+    }
     const int tile = ((x | 7) < tiles_per_row) ? ((x & ~7) | ((x + b) & 7)) : x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wv = __builtin_amdgcn_readfirstlane(wave);     // wave-uniform
@@ -301,22 +320,28 @@ hipError_t launch_index_scores(const IndexParams &prm, int D, int B, hipStream_t
     const bool wide = prm.Hkv >= 8 && wgs * kIndexWaves < 2 * 4 * kIndexCUs;
     // at most 8 q heads per KV head: one pass per KV head, the key converted chunk by chunk
     const bool oneg = prm.Hq <= kHeadGroup * prm.Hkv;
+    // large grids whose rows have several aligned groups of 8 tiles start them group by group
+    const bool ord = !wide && grid.x > 8 && grid.x % 8 == 0;
     auto go = [&](auto kern, int nw) { kern<<<grid, nw * 64, 0, stream>>>(prm); };
     if (D == 64) {
         if (oneg) {
-            if (wide) go(index_scores_kernel<64, 8, true>, 8);
-            else go(index_scores_kernel<64, kIndexWaves, true>, kIndexWaves);
+            if (wide) go(index_scores_kernel<64, 8, true, false>, 8);
+            else if (ord) go(index_scores_kernel<64, kIndexWaves, true, true>, kIndexWaves);
+            else go(index_scores_kernel<64, kIndexWaves, true, false>, kIndexWaves);
         } else {
-            if (wide) go(index_scores_kernel<64, 8, false>, 8);
-            else go(index_scores_kernel<64, kIndexWaves, false>, kIndexWaves);
+            if (wide) go(index_scores_kernel<64, 8, false, false>, 8);
+            else if (ord) go(index_scores_kernel<64, kIndexWaves, false, true>, kIndexWaves);
+            else go(index_scores_kernel<64, kIndexWaves, false, false>, kIndexWaves);
         }
     } else {
         if (oneg) {
-            if (wide) go(index_scores_kernel<128, 8, true>, 8);
-            else go(index_scores_kernel<128, kIndexWaves, true>, kIndexWaves);
+            if (wide) go(index_scores_kernel<128, 8, true, false>, 8);
+            else if (ord) go(index_scores_kernel<128, kIndexWaves, true, true>, kIndexWaves);
+            else go(index_scores_kernel<128, kIndexWaves, true, false>, kIndexWaves);
         } else {
-            if (wide) go(index_scores_kernel<128, 8, false>, 8);
-            else go(index_scores_kernel<128, kIndexWaves, false>, kIndexWaves);
+            if (wide) go(index_scores_kernel<128, 8, false, false>, 8);
+            else if (ord) go(index_scores_kernel<128, kIndexWaves, false, true>, kIndexWaves);
+            else go(index_scores_kernel<128, kIndexWaves, false, false>, kIndexWaves);
         }
     }
     return hipGetLastError();

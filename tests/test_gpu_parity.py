@@ -106,6 +106,13 @@ SMALL = [
     synth.Config("s_hkv8_g12", 2, 1, 96, 8, 128, 64, (200, 2000), 4, 1, seed=107, invalid_frac=0.05),
     # a large grid (6400 waves) with an odd number of rows per request
     synth.Config("s_rows5_large", 64, 5, 16, 2, 64, 64, (3000, 20000), 8, 1, seed=108, invalid_frac=0.05),
+    # rows of 16 and 24 page tiles (two and three aligned groups of 8), whose index launch starts
+    # the tile groups one after another: batches that are not a multiple of 8, and short
+    # requests whose later groups hold no page; one pass per KV head and (12 q heads per KV
+    # head) two head groups
+    synth.Config("s_ord_16tiles", 5, 3, 16, 4, 128, 64, (200, 60000), 6, 2, seed=111, invalid_frac=0.05,
+                 max_pages=1024),
+    synth.Config("s_ord_24tiles_g12", 3, 2, 24, 2, 64, 64, (100, 95000), 5, 1, seed=112, max_pages=1536),
 ]
 CONFIG_NAMES = list(synth.CONFIGS)
 
