@@ -104,13 +104,14 @@ __global__ __launch_bounds__(NW * 64, ONEG ? kOnePassWaves : 2) void index_score
     int j = blockIdx.y, b = blockIdx.z, x = blockIdx.x;
     if constexpr (ORD) {
         // grid (tiles_per_row, rmax, B), tiles_per_row = 8m: id = x + tiles * (j + rmax * b);
-        // id mod 8 = x mod 8, and id / 8 = group * (rmax * B) + (j + rmax * b) afterwards
+        // id mod 8 = x mod 8, and id / 8 = group * (rmax * B) + (j + rmax * b) afterwards. The
+        // id is unsigned: up to 64 tiles x 1024 rows x 65535 requests, just under 2^32.
         const int RB = prm.rmax * (int)gridDim.z;
-        const int lin = x + tiles_per_row * (j + prm.rmax * b);
-        const int slot = lin >> 3, grp = slot / RB, rem = slot - grp * RB;
+        const uint32_t lin = (uint32_t)x + (uint32_t)tiles_per_row * ((uint32_t)j + (uint32_t)prm.rmax * (uint32_t)b);
+        const int slot = (int)(lin >> 3), grp = slot / RB, rem = slot - grp * RB;
         b = rem / prm.rmax;
         j = rem - b * prm.rmax;
-        x = grp * 8 + (lin & 7);
+        x = grp * 8 + (int)(lin & 7u);
     }
     const int tile = ((x | 7) < tiles_per_row) ? ((x & ~7) | ((x + b) & 7)) : x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
